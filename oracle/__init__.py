@@ -1,0 +1,10 @@
+"""CPU oracle for the approximate-attention prefill path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU baseline, never by the product library.
+"""
+from .spava_oracle import (  # noqa: F401
+    split_sequence, block_scores, select_passing, gather_passing, attend,
+    anchor_rows, context_rows, query_partials, lse_merge, approx_prefill,
+    sampled_rows, dense_causal,
+)
