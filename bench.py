@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of one approximate-attention prefill layer on one MI355X.
+
+A step is one pass of the whole path on inputs already resident in HBM:
+spava_score_topk -> spava_gather_passing -> spava_attn_fwd -> spava_lse_merge.
+Workload: Qwen2.5-VL-3B-like attention at 32K tokens (16 query / 2 KV heads,
+d=128; anchor 2048; 8 virtual hosts x 3840; query 128; lp=1024), bf16.
+
+Prints ONE JSON line.  Besides the throughput it reports the roofline of the
+dominant call (the fused attention) from HIP events recorded on the stream
+the library launches on, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "approx-attention prefill tokens/s per layer; TFLOP/s and % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def attn_pairs_per_head(w, lp=None) -> int:
+    """Unmasked (query, key) pairs of one query head over the whole layer."""
+    la, V, L, nq = w.n_anchor, w.n_hosts, w.host_len, w.n_query
+    lp = w.lp if lp is None else lp
+    anchor = la * (la + 1) // 2
+    context = sum(L * (la + h * lp) + L * (L + 1) // 2 for h in range(V))
+    query = nq * la + nq * (nq + 1) // 2 + V * nq * L
+    return anchor + context + query
+
+
+def attn_flops(w) -> float:
+    return 4.0 * w.head_dim * w.n_q_heads * attn_pairs_per_head(w)
+
+
+def score_flops(w) -> float:
+    """One Q K^T pass of the query rows over every block (both score passes
+    recompute it; only one is counted as algorithmic work)."""
+    return 2.0 * w.head_dim * (w.n_query * w.n_q_heads) * (w.n_hosts * w.host_len)
+
+
+def cpu_baseline(w, x):
+    """The oracle as it stands, on a bounded sample of the same layer:
+    scoring + selection in full, then the context rows of hosts 0 and V-1
+    for the query heads of one KV group; the attention time is extrapolated
+    to the whole layer by its share of attention pairs."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    la, V, L, nq, lp = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.lp
+    t0 = time.perf_counter()
+    sc = O.block_scores(x["q"], x["k"], la, V, L, nq)
+    idx = O.select_passing(sc, lp)
+    kp, vp = O.gather_passing(x["k"], x["v"], idx, la, L)
+    t1 = time.perf_counter()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    G = w.group
+    for h in (0, V - 1):                    # the query heads of KV group 0
+        O.context_rows(x["q"][:, :G], x["k"][:, :1], x["v"][:, :1], kp[:1], vp[:1], la, V, L, h, scale)
+    t2 = time.perf_counter()
+    sample_pairs = G * sum(L * (la + h * lp) + L * (L + 1) // 2 for h in (0, V - 1))
+    total_pairs = attn_pairs_per_head(w) * w.n_q_heads
+    t_layer = (t1 - t0) + (t2 - t1) * total_pairs / sample_pairs
+    return {
+        "value": w.n_tokens / t_layer,
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: scores+top-lp+gather of the full layer ({t1 - t0:.1f} s), "
+                   f"then context rows of hosts 0 and {V - 1} for {G} of {w.n_q_heads} query heads "
+                   f"({t2 - t1:.1f} s); attention extrapolated by pair count "
+                   f"({total_pairs / sample_pairs:.1f}x) to {t_layer:.1f} s per layer"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the virtual hosts are batched on a single device).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sequence_approximate_attention_amd as S
+    import workloads as W
+
+    wl = {w.name: w for w in W.WORKLOADS}[args.workload]
+    x = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = S.plan_for(wl)
+    to = lambda n: torch.from_numpy(x[n + "16"].view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to("q"), to("k"), to("v")
+    bufs = S.alloc_buffers(plan, dev)
+    stream = torch.cuda.current_stream()
+    q0 = wl.n_anchor + wl.n_hosts * wl.host_len
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        S.spava_score_topk(plan, q, k, bufs.scores, bufs.idx, bufs.ws_score, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        S.spava_attn_fwd(plan, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse, bufs.o_part,
+                         bufs.lse_part, bufs.ws_attn, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        S.spava_lse_merge(bufs.o_part, bufs.lse_part, bufs.o[q0:], plan.n_q_heads * plan.head_dim,
+                          bufs.lse[:, q0:], plan.n_tokens, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stage = {"score_topk": [], "gather": [], "attn_fwd": [], "lse_merge": []}
+    for ev in events:
+        stage["score_topk"].append(ev[0].elapsed_time(ev[1]))
+        stage["gather"].append(ev[1].elapsed_time(ev[2]))
+        stage["attn_fwd"].append(ev[2].elapsed_time(ev[3]))
+        stage["lse_merge"].append(ev[3].elapsed_time(ev[4]))
+    stage_ms = {kk: float(np.mean(vv)) for kk, vv in stage.items()}
+    attn_ms = stage_ms["attn_fwd"]
+    F_attn = attn_flops(wl)
+    achieved = F_attn / (attn_ms * 1e-3) / 1e12
+    tokens_per_s = wl.n_tokens / (ms_per_step * 1e-3)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.n_tokens, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "anchor": wl.n_anchor,
+                   "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "attn_tflop_per_launch": F_attn / 1e12,
+        "step_tflops": (F_attn + score_flops(wl)) / (ms_per_step * 1e-3) / 1e12,
+        "stage_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * spava.h -- C ABI of the approximate-attention prefill library (gfx950).
+ *
+ * The library computes one transformer layer's prefill attention the way
+ * "Spava / APB-V: Accelerating Long-Video Understanding via
+ * Sequence-Parallelism-aware Approximate Attention" describes it, with all
+ * virtual hosts' context blocks on one GPU:
+ *
+ *   token rows  = [ anchor (la) | block 0 (L) | ... | block V-1 (L) | query (n_q) ]
+ *                 (Figure 2 caption: B_a, B^(h), B_qr)
+ *   1. spava_score_topk      score every key of every block by the query
+ *                            block's attention and keep the top lp per block
+ *                            and KV head (Figure 5 caption; review "What
+ *                            carries the argument"; ledger axiom on ArgTop_lp)
+ *   2. spava_gather_passing  copy the kept K,V rows into passing blocks
+ *                            (Figure 2 caption: blocks compressed, then passed)
+ *   3. spava_attn_fwd        anchor and context tokens attend over anchor +
+ *                            earlier hosts' passing blocks + own block
+ *                            (review "Core claim"; Referee Report, Eq. (4));
+ *                            query tokens produce one partial per key group in
+ *                            the same pass (Figure 3 caption: fused context
+ *                            and query forward)
+ *   4. spava_lse_merge       merge the query partials through their
+ *                            log-sum-exp (ledger axiom: Eq. 5, Appendix A)
+ *
+ * Conventions shared by every call
+ *   - Pointers named q, k, v, kp, vp, o, lse, o_part, lse_part, scores, idx
+ *     and ws are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises; every call only enqueues work on
+ *     `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *   - All tensors are dense and row-major in the layouts stated below, and
+ *     must be 16-byte aligned.
+ *   - Return value: SPAVA_OK or an error code.  Argument checks run on the
+ *     host before anything is enqueued; on an error nothing is enqueued and
+ *     spava_last_error() (per thread) describes it.  A launch failure
+ *     returns SPAVA_ELAUNCH.
+ *   - Identical inputs give bitwise-identical outputs (no atomics on values).
+ *   - Q and K are taken after any positional encoding; none is applied.
+ *   - Query head a uses KV head a / (n_q_heads / n_kv_heads).
+ */
+#ifndef SPAVA_H
+#define SPAVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPAVA_VERSION 100
+
+#define SPAVA_OK 0
+#define SPAVA_EINVAL 1        /* null pointer, bad size, misaligned pointer   */
+#define SPAVA_EUNSUPPORTED 2  /* head_dim other than 64/128, unknown dtype    */
+#define SPAVA_EWORKSPACE 3    /* workspace smaller than the *_ws_bytes size    */
+#define SPAVA_ELAUNCH 4       /* a kernel launch failed                        */
+
+#define SPAVA_BF16 0          /* bfloat16 inputs, float32 arithmetic           */
+#define SPAVA_F32 1           /* float32 inputs, float32 arithmetic            */
+
+/*
+ * One layer's sequence split (Figure 2 caption) and head geometry.
+ *   n_anchor   la  >= 0   anchor tokens (first la rows)
+ *   n_hosts    V   >= 1   virtual hosts (context blocks)
+ *   host_len   L   >= 1   tokens per context block
+ *   n_query    n_q >= 0   query-block tokens (last n_q rows)
+ *   n_q_heads, n_kv_heads  Hq % Hkv == 0
+ *   head_dim   d   64 or 128
+ *   lp             passing length, 0 <= lp <= L
+ *   dtype          SPAVA_BF16 or SPAVA_F32 (element type of q,k,v,kp,vp,o)
+ *   scale          softmax scale; 0 means 1/sqrt(d)
+ * N = la + V*L + n_q rows in total; N * max(Hq, Hkv) * d must be < 2^31.
+ */
+typedef struct spava_plan {
+  int32_t n_anchor;
+  int32_t n_hosts;
+  int32_t host_len;
+  int32_t n_query;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t lp;
+  int32_t dtype;
+  float scale;
+} spava_plan;
+
+/* SPAVA_VERSION of the built library. */
+int spava_version(void);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* spava_last_error(void);
+
+/* Host-only check of a plan; returns SPAVA_OK or the code a call would. */
+int spava_plan_check(const spava_plan* plan);
+
+/*
+ * Workspace bytes spava_score_topk needs: the per-row log-sum-exp of the
+ * query rows over each block, float32 [V][Hkv][n_q*G], rounded up.
+ */
+size_t spava_score_topk_ws_bytes(const spava_plan* plan);
+
+/*
+ * Step 1: block scores and top-lp selection.
+ * Scoring rule (Figure 5 caption: Q_qr K^(h)T estimates KV importance): for
+ * block h and KV head g,
+ *     scores[h][g][j] = sum over query tokens i and query heads a of group g
+ *                       of softmax_j( q[la+V*L+i][a] . k[la+h*L+j][g] * scale )
+ * with the softmax over the L keys of block h only.  Selection (ledger axiom:
+ * ArgTop_lp): the lp indices first in the order (score descending, index
+ * ascending), written in ascending order.
+ *   q       [N][Hq][d]      dtype
+ *   k       [N][Hkv][d]     dtype
+ *   scores  [V][Hkv][L]     float32, written (also useful as a diagnostic)
+ *   idx     [V][Hkv][lp]    int32 block-local key indices, written
+ *   ws      >= spava_score_topk_ws_bytes(plan) bytes of scratch
+ * With n_q == 0 every score is 0 and idx = 0..lp-1.
+ */
+int spava_score_topk(const spava_plan* plan, const void* q, const void* k,
+                     float* scores, int32_t* idx, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * Step 2: passing blocks (Figure 2 caption).
+ *   kp[g][h][t][:] = k[la + h*L + idx[h][g][t]][g][:]
+ *   vp[g][h][t][:] = v[la + h*L + idx[h][g][t]][g][:]
+ *   k, v    [N][Hkv][d]        dtype
+ *   idx     [V][Hkv][lp]       int32, each in [0, L) (not checked on device;
+ *                              an out-of-range index is clamped into the block)
+ *   kp, vp  [Hkv][V][lp][d]    dtype, written
+ * kp/vp may be reused once the stream has passed spava_attn_fwd (the pages
+ * discard passing blocks right after attention).
+ */
+int spava_gather_passing(const spava_plan* plan, const void* k, const void* v,
+                         const int32_t* idx, void* kp, void* vp, void* stream);
+
+/*
+ * Workspace bytes spava_attn_fwd needs: key-contiguous copies of V and of the
+ * passing values, padded per segment to the kernel's key tile.
+ */
+size_t spava_attn_fwd_ws_bytes(const spava_plan* plan);
+
+/*
+ * Step 3: fused approximate attention forward (Figure 3 caption; review
+ * "Core claim"; Referee Report, Eq. (4) key list [K_a, K_p, K^(h)]).
+ *   anchor token t < la:           keys 0..t                       (causal)
+ *   context token t of host h:     keys anchor, kp/vp[g][0..h-1],
+ *                                  own block rows <= t              (causal)
+ *   query partial 0:               keys anchor, query rows <= t     (causal)
+ *   query partial h+1:             keys of block h                  (all)
+ * Softmax with the plan's scale; LSE is the natural log of the sum of
+ * exp(scaled logits).
+ *   q [N][Hq][d]; k, v [N][Hkv][d]; kp, vp [Hkv][V][lp][d]      dtype
+ *   o         [N][Hq][d]          dtype; rows [0, la+V*L) written
+ *   lse       [Hq][N]             float32; columns [0, la+V*L) written
+ *   o_part    [V+1][n_q][Hq][d]   float32, written (may be NULL if n_q == 0)
+ *   lse_part  [V+1][Hq][n_q]      float32, written (may be NULL if n_q == 0)
+ *   ws        >= spava_attn_fwd_ws_bytes(plan) bytes of scratch
+ * Dense causal attention is the plan {la=0, V=1, L=N, n_q=0, lp=0}
+ * (one host degrades to standard attention).
+ */
+int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k,
+                   const void* v, const void* kp, const void* vp, void* o,
+                   float* lse, float* o_part, float* lse_part, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * Step 4: log-sum-exp merge of partial attention results (ledger axiom,
+ * Eq. 5 / Appendix A).  For row r, head a:
+ *     m   = max_p lse_part[p][a][r]
+ *     w_p = exp(lse_part[p][a][r] - m)
+ *     o[r*o_row_stride + a*head_dim + c] = sum_p w_p o_part[p][r][a][c] / sum_p w_p
+ *     lse[a*lse_head_stride + r]          = m + log(sum_p w_p)
+ * If every partial has lse = -inf the row gets o = 0 and lse = -inf.
+ *   o_part    [n_parts][n_rows][n_heads][head_dim]  float32
+ *   lse_part  [n_parts][n_heads][n_rows]            float32
+ *   o         out_dtype (SPAVA_BF16 or SPAVA_F32), strided as above
+ *   lse       float32, strided as above
+ * For the query rows of spava_attn_fwd: n_parts = V+1, n_rows = n_q,
+ * o = o + (la+V*L)*Hq*d with o_row_stride = Hq*d, lse = lse + (la+V*L) with
+ * lse_head_stride = N.
+ */
+int spava_lse_merge(int32_t n_parts, int32_t n_rows, int32_t n_heads,
+                    int32_t head_dim, const float* o_part, const float* lse_part,
+                    void* o, int64_t o_row_stride, float* lse,
+                    int64_t lse_head_stride, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPAVA_H */

@@ -74,8 +74,6 @@ def block_scores(q, k, la, V, L, n_q, scale=None):
 
     q: [N, Hq, d], k: [N, Hkv, d].  Returns float64 [V, Hkv, L].
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
     Hq, d = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -83,12 +81,13 @@ def block_scores(q, k, la, V, L, n_q, scale=None):
         scale = 1.0 / math.sqrt(d)
     seg = split_sequence(la, V, L, n_q)
     q0, q1 = seg["query"]
+    qq = np.asarray(q[q0:q1], dtype=np.float64)                    # query block only
     out = np.zeros((V, Hkv, L), dtype=np.float64)
     for h, (b0, b1) in enumerate(seg["blocks"]):
         for g in range(Hkv):
-            keys = k[b0:b1, g, :]                                  # [L, d]
+            keys = np.asarray(k[b0:b1, g, :], dtype=np.float64)    # [L, d]
             for a in range(g * G, (g + 1) * G):
-                rows = q[q0:q1, a, :]                              # [n_q, d]
+                rows = qq[:, a, :]                                 # [n_q, d]
                 s = (rows @ keys.T) * scale                        # [n_q, L]
                 s = s - s.max(axis=1, keepdims=True)
                 p = np.exp(s)
@@ -318,47 +317,61 @@ def sampled_rows(q, k, v, kp, vp, la, V, L, n_q, rows, scale=None):
     """Outputs of chosen (token, head) pairs, computed one by one.
 
     For full-size workloads where the whole oracle is too slow.  Each row is
-    computed from its own key list exactly as in ``approx_prefill``; query
-    tokens go through their V+1 partials and the merge.
+    computed from its own key list exactly as in ``approx_prefill``: the key
+    list of a context token of host h is [anchor, passing blocks 0..h-1,
+    own block up to the token] -- the causal part is a prefix of host h's
+    full list, built once per (KV head, host).  Query tokens go through
+    their V+1 partials and the merge.  Inputs are converted to float64 one
+    KV head at a time.
     Returns O [len(rows), d], LSE [len(rows)].
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    kp = np.asarray(kp, dtype=np.float64)
-    vp = np.asarray(vp, dtype=np.float64)
     Hq, d = q.shape[1], q.shape[2]
-    G = Hq // k.shape[1]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
     lp = kp.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     q0 = la + V * L
     outO = np.zeros((len(rows), vp.shape[-1]))
     outL = np.zeros(len(rows))
-    for n, (t, a) in enumerate(rows):
-        g = a // G
-        qr = q[t, a][None, :]
-        if t < la:                                                  # anchor token
-            o, lse = attend(qr, k[:t + 1, g], v[:t + 1, g], np.ones((1, t + 1), bool), scale)
-        elif t < q0:                                                # context token of host h
-            h = (t - la) // L
-            b0 = la + h * L
-            keys = np.concatenate([k[:la, g], kp[g, :h].reshape(h * lp, d), k[b0:t + 1, g]], axis=0)
-            vals = np.concatenate([v[:la, g], vp[g, :h].reshape(h * lp, vp.shape[-1]), v[b0:t + 1, g]], axis=0)
-            o, lse = attend(qr, keys, vals, np.ones((1, keys.shape[0]), bool), scale)
-        else:                                                       # query token: partials + merge
-            parts_o, parts_l = [], []
-            keys = np.concatenate([k[:la, g], k[q0:t + 1, g]], axis=0)
-            vals = np.concatenate([v[:la, g], v[q0:t + 1, g]], axis=0)
-            o0, l0 = attend(qr, keys, vals, np.ones((1, keys.shape[0]), bool), scale)
-            parts_o.append(o0[0]); parts_l.append(l0[0])
-            for h in range(V):
+    for g in range(Hkv):
+        mine = [n for n, (t, a) in enumerate(rows) if a // G == g]
+        if not mine:
+            continue
+        kg = np.asarray(k[:, g], dtype=np.float64)
+        vg = np.asarray(v[:, g], dtype=np.float64)
+        kpg = np.asarray(kp[g], dtype=np.float64).reshape(V * lp, d)
+        vpg = np.asarray(vp[g], dtype=np.float64).reshape(V * lp, -1)
+        host_lists = {}
+        for n in sorted(mine, key=lambda n: rows[n][0]):
+            t, a = rows[n]
+            qr = np.asarray(q[t, a], dtype=np.float64)[None, :]
+            if t < la:                                              # anchor token
+                keys, vals = kg[:t + 1], vg[:t + 1]
+            elif t < q0:                                            # context token of host h
+                h = (t - la) // L
                 b0 = la + h * L
-                oh, lh = attend(qr, k[b0:b0 + L, g], v[b0:b0 + L, g], np.ones((1, L), bool), scale)
-                parts_o.append(oh[0]); parts_l.append(lh[0])
-            o, lse = lse_merge(np.stack(parts_o)[:, None, :], np.stack(parts_l)[:, None])
-        outO[n] = o[0]
-        outL[n] = lse[0]
+                if h not in host_lists:
+                    host_lists = {h: (
+                        np.concatenate([kg[:la], kpg[:h * lp], kg[b0:b0 + L]], axis=0),
+                        np.concatenate([vg[:la], vpg[:h * lp], vg[b0:b0 + L]], axis=0))}
+                n_vis = la + h * lp + (t - b0) + 1
+                keys, vals = host_lists[h][0][:n_vis], host_lists[h][1][:n_vis]
+            else:                                                   # query token: partials + merge
+                parts_o, parts_l = [], []
+                keys = np.concatenate([kg[:la], kg[q0:t + 1]], axis=0)
+                vals = np.concatenate([vg[:la], vg[q0:t + 1]], axis=0)
+                o0, l0 = attend(qr, keys, vals, np.ones((1, keys.shape[0]), bool), scale)
+                parts_o.append(o0[0]); parts_l.append(l0[0])
+                for h in range(V):
+                    b0 = la + h * L
+                    oh, lh = attend(qr, kg[b0:b0 + L], vg[b0:b0 + L], np.ones((1, L), bool), scale)
+                    parts_o.append(oh[0]); parts_l.append(lh[0])
+                o, lse = lse_merge(np.stack(parts_o)[:, None, :], np.stack(parts_l)[:, None])
+                outO[n], outL[n] = o[0], lse[0]
+                continue
+            o, lse = attend(qr, keys, vals, np.ones((1, keys.shape[0]), bool), scale)
+            outO[n], outL[n] = o[0], lse[0]
     return outO, outL
 
 

@@ -1,0 +1,64 @@
+"""Build libspava.so for gfx950 with hipcc (in-tree, next to this file).
+
+Usage: python -m sequence_approximate_attention_amd.build   (or build())
+Every call recompiles all sources.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libspava.so")
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "score.hip", "aux.hip"]
+ARCH = os.environ.get("SPAVA_ARCH", "gfx950")
+
+# Packed-FP32 instructions are disabled for the device code: plain float math
+# only (the flag is a device-side target feature; the host pass ignores it).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str, obj: str, extra: list[str]) -> None:
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
+           os.path.join(CSRC, src), "-o", obj, *DEVICE_FLAGS, *extra]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if l.strip() and noise not in l]
+    if msgs:
+        sys.stderr.write("\n".join(msgs) + "\n")
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile every HIP source and link libspava.so; returns its path."""
+    extra = list(extra or [])
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(SOURCES, objs)))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,236 @@
+// C ABI of libspava: argument checks and launch sequencing (see include/spava.h).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "spava_common.h"
+
+namespace spava {
+namespace {
+
+constexpr int kRowsPerUnit = 128;  // query rows per attention workgroup (both paths)
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_plan(const spava_plan* p) {
+  if (!p) return fail(SPAVA_EINVAL, "plan is NULL");
+  if (p->dtype != SPAVA_BF16 && p->dtype != SPAVA_F32)
+    return fail(SPAVA_EUNSUPPORTED, "dtype %d is not SPAVA_BF16 or SPAVA_F32", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SPAVA_EUNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (p->n_anchor < 0 || p->n_hosts < 1 || p->host_len < 1 || p->n_query < 0)
+    return fail(SPAVA_EINVAL, "need n_anchor>=0, n_hosts>=1, host_len>=1, n_query>=0");
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1 || p->n_q_heads % p->n_kv_heads != 0)
+    return fail(SPAVA_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->lp < 0 || p->lp > p->host_len)
+    return fail(SPAVA_EINVAL, "lp (%d) must lie in [0, host_len=%d]", p->lp, p->host_len);
+  if (!(p->scale >= 0.0f) || isinf(p->scale))
+    return fail(SPAVA_EINVAL, "scale must be finite and >= 0 (0 = 1/sqrt(d))");
+  const double N = (double)p->n_anchor + (double)p->n_hosts * p->host_len + p->n_query;
+  const double H = p->n_q_heads > p->n_kv_heads ? p->n_q_heads : p->n_kv_heads;
+  if (N * H * p->head_dim >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "N*heads*head_dim must stay below 2^31");
+  if ((double)p->n_hosts * p->lp * p->n_kv_heads * p->head_dim >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "passing blocks too large");
+  return SPAVA_OK;
+}
+
+AttnArgs make_args(const spava_plan* p) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Hq = p->n_q_heads;
+  a.Hkv = p->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.D = p->head_dim;
+  a.la = p->n_anchor;
+  a.V = p->n_hosts;
+  a.L = p->host_len;
+  a.nq = p->n_query;
+  a.lp = p->lp;
+  a.N = a.la + a.V * a.L + a.nq;
+  a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)a.D);
+  a.scale_log2 = a.scale * 1.44269504088896340736f;
+  a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
+  a.rows_per_unit = kRowsPerUnit;
+  a.n_ctx_units_per_host = ceil_div(a.L, kRowsPerUnit) * a.Hq;
+  a.n_q_units = ceil_div(a.nq * a.G, kRowsPerUnit) * a.Hkv;
+  a.n_anchor_units = ceil_div(a.la, kRowsPerUnit) * a.Hq;
+  a.f32 = p->dtype == SPAVA_F32;
+  return a;
+}
+
+size_t stats_bytes(const spava_plan* p) {
+  const size_t R = (size_t)p->n_query * (p->n_q_heads / p->n_kv_heads);
+  return ((size_t)p->n_hosts * p->n_kv_heads * R * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
+  const VtLayout vl = VtLayout::make(p->n_anchor, p->n_hosts, p->host_len, p->n_query, p->lp);
+  const size_t main = (size_t)p->n_kv_heads * p->head_dim * vl.main_len * 2;
+  const size_t pass = (size_t)p->n_kv_heads * p->head_dim * vl.pass_len * 2;
+  const size_t main_al = (main + 255) / 256 * 256;
+  if (off_pass) *off_pass = main_al;
+  return main_al + (pass + 255) / 256 * 256;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPAVA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SPAVA_OK;
+}
+
+}  // namespace
+}  // namespace spava
+
+using namespace spava;
+
+extern "C" {
+
+int spava_version(void) { return SPAVA_VERSION; }
+
+const char* spava_last_error(void) { return g_err; }
+
+int spava_plan_check(const spava_plan* plan) {
+  int rc = check_plan(plan);
+  if (rc == SPAVA_OK) g_err[0] = 0;
+  return rc;
+}
+
+size_t spava_score_topk_ws_bytes(const spava_plan* plan) {
+  if (check_plan(plan) != SPAVA_OK) return 0;
+  return stats_bytes(plan);
+}
+
+int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float* scores,
+                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  if (!q || !k || !scores || !ws || (plan->lp > 0 && !idx))
+    return fail(SPAVA_EINVAL, "spava_score_topk: q, k, scores, ws (and idx when lp > 0) must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) || (idx && !aligned16(idx)))
+    return fail(SPAVA_EINVAL, "spava_score_topk: pointers must be 16-byte aligned");
+  if (ws_bytes < stats_bytes(plan))
+    return fail(SPAVA_EWORKSPACE, "spava_score_topk: workspace %zu < %zu bytes", ws_bytes, stats_bytes(plan));
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a = make_args(plan);
+  a.q = q;
+  a.k = k;
+  a.stats = (float*)ws;
+  hipError_t e = hipSuccess;
+  if (a.nq > 0) {
+    if (a.f32) {
+      e = launch_rowstat_f32(a, s);
+    } else {
+      a.stats_only = 1;
+      e = launch_attn_bf16(a, s);
+    }
+    if (e != hipSuccess) return launched(e, "row statistics");
+  }
+  e = launch_colsum(a, scores, s);
+  if (e != hipSuccess) return launched(e, "column sums");
+  e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);
+  return launched(e, "top-lp selection");
+}
+
+int spava_gather_passing(const spava_plan* plan, const void* k, const void* v, const int32_t* idx,
+                         void* kp, void* vp, void* stream) {
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  if (plan->lp == 0) {
+    g_err[0] = 0;
+    return SPAVA_OK;
+  }
+  if (!k || !v || !idx || !kp || !vp)
+    return fail(SPAVA_EINVAL, "spava_gather_passing: NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kp) || !aligned16(vp))
+    return fail(SPAVA_EINVAL, "spava_gather_passing: pointers must be 16-byte aligned");
+  const int esz = plan->dtype == SPAVA_F32 ? 4 : 2;
+  hipError_t e = launch_gather(k, v, idx, kp, vp, plan->n_anchor, plan->n_hosts, plan->host_len,
+                               plan->n_kv_heads, plan->lp, plan->head_dim * esz, (hipStream_t)stream);
+  return launched(e, "gather");
+}
+
+size_t spava_attn_fwd_ws_bytes(const spava_plan* plan) {
+  if (check_plan(plan) != SPAVA_OK) return 0;
+  if (plan->dtype == SPAVA_F32) return 256;
+  return vt_bytes(plan, nullptr);
+}
+
+int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k, const void* v,
+                   const void* kp, const void* vp, void* o, float* lse, float* o_part,
+                   float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  const bool need_pass = plan->lp > 0 && plan->n_hosts > 1;
+  if (!q || !k || !v || !o || !lse || !ws || (need_pass && (!kp || !vp)) ||
+      (plan->n_query > 0 && (!o_part || !lse_part)))
+    return fail(SPAVA_EINVAL, "spava_attn_fwd: NULL pointer");
+  const void* ptrs[] = {q, k, v, kp, vp, o, lse, o_part, lse_part, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SPAVA_EINVAL, "spava_attn_fwd: pointers must be 16-byte aligned");
+  const size_t need = spava_attn_fwd_ws_bytes(plan);
+  if (ws_bytes < need)
+    return fail(SPAVA_EWORKSPACE, "spava_attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a = make_args(plan);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kp = kp;
+  a.vp = vp;
+  a.o = o;
+  a.lse = lse;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  hipError_t e;
+  if (a.f32) {
+    e = launch_attn_f32(a, s);
+    return launched(e, "attention (float32)");
+  }
+  size_t off_pass = 0;
+  vt_bytes(plan, &off_pass);
+  uint16_t* vt = (uint16_t*)ws;
+  uint16_t* vpt = (uint16_t*)((char*)ws + off_pass);
+  e = launch_vtranspose(a, vt, vpt, s);
+  if (e != hipSuccess) return launched(e, "V transpose");
+  a.vt = vt;
+  a.vpt = vpt;
+  e = launch_attn_bf16(a, s);
+  return launched(e, "attention (bf16)");
+}
+
+int spava_lse_merge(int32_t n_parts, int32_t n_rows, int32_t n_heads, int32_t head_dim,
+                    const float* o_part, const float* lse_part, void* o, int64_t o_row_stride,
+                    float* lse, int64_t lse_head_stride, int32_t out_dtype, void* stream) {
+  if (n_parts < 1 || n_rows < 0 || n_heads < 1 || head_dim < 4 || head_dim % 4 != 0)
+    return fail(SPAVA_EINVAL, "spava_lse_merge: need n_parts>=1, n_rows>=0, n_heads>=1, head_dim%%4==0");
+  if (out_dtype != SPAVA_BF16 && out_dtype != SPAVA_F32)
+    return fail(SPAVA_EUNSUPPORTED, "spava_lse_merge: out_dtype %d", out_dtype);
+  if (n_rows == 0) {
+    g_err[0] = 0;
+    return SPAVA_OK;
+  }
+  if (!o_part || !lse_part || !o || !lse) return fail(SPAVA_EINVAL, "spava_lse_merge: NULL pointer");
+  if (!aligned16(o_part) || ((uintptr_t)o & (out_dtype == SPAVA_F32 ? 15u : 7u)) ||
+      (o_row_stride % 4) != 0 || ((uintptr_t)lse & 3u))
+    return fail(SPAVA_EINVAL, "spava_lse_merge: misaligned pointer or row stride");
+  if (o_row_stride < (int64_t)n_heads * head_dim || lse_head_stride < n_rows)
+    return fail(SPAVA_EINVAL, "spava_lse_merge: strides too small");
+  hipError_t e = launch_merge(n_parts, n_rows, n_heads, head_dim, o_part, lse_part, o, o_row_stride,
+                              lse, lse_head_stride, out_dtype == SPAVA_BF16, (hipStream_t)stream);
+  return launched(e, "merge");
+}
+
+}  // extern "C"

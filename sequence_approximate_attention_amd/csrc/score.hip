@@ -1,0 +1,340 @@
+// Block scoring and top-lp selection.
+//
+// Scoring (Figure 5 caption of the Spava page: Q_qr K^(h)T estimates KV
+// importance; "What carries the argument" in the APB-V review: keys ranked by
+// query-to-context attention scores).  For block h and KV head g the score of
+// key j is the sum over the query block's rows r = (token i, head a in g) of
+// softmax_j(q_r . k_j * scale) over the block's L keys.  It takes two passes
+// over the block: the row log-sum-exp (the attention kernel's statistics
+// mode, or rowstat_f32 below), then the column sums here.  Probabilities are
+// float32, column sums accumulate in float64 in a fixed order, so the result
+// is deterministic and its relative error stays far below 1e-6.
+//
+// Selection (ArgTop_lp in the APB-V review's axiom ledger): an exact radix
+// select on the order-preserving integer image of the float32 scores finds
+// the lp-th largest value; ties at that value go to the lower indices; the
+// kept indices are written in ascending order by a block-wide prefix sum.
+#include "spava_common.h"
+
+namespace spava {
+namespace {
+
+constexpr int kColThreads = 256;
+constexpr int kColKeys = 256;  // keys per workgroup (64 per wave)
+
+// S = Q K^T with the packed query rows as the A operand and the workgroup's
+// keys as the B operand (each wave holds 64 keys' fragments in registers);
+// Q tiles of 32 rows and their log2-domain LSE are staged in LDS.
+template <int D>
+__global__ __launch_bounds__(kColThreads) void colsum_bf16_kernel(AttnArgs a, float* __restrict__ scores) {
+  constexpr int NC = D / 16;
+  constexpr int QS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * QS];
+  __shared__ float sL[32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  const int hg = blockIdx.y;  // h * Hkv + g
+  const int h = hg / a.Hkv;
+  const int g = hg % a.Hkv;
+  const int R = a.nq * a.G;
+  const long kstr = (long)a.Hkv * D;
+  const int key0 = blockIdx.x * kColKeys + wave * 64;
+  const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
+
+  bf16x8 kf[2][NC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = min(key0 + 32 * kb + col, a.L - 1);
+    const uint16_t* kr = kbase + (long)j * kstr + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kf[kb][c] = *(const bf16x8*)(kr + 16 * c);
+  }
+  double acc[2] = {0.0, 0.0};
+  const float sl2 = a.scale_log2;
+  const float* lse2 = a.stats + (long)hg * R;
+  const int q0 = a.la + a.V * a.L;
+
+  for (int r0 = 0; r0 < R; r0 += 32) {
+    __syncthreads();
+    constexpr int CPR = D / 8;
+    for (int ch = tid; ch < 32 * CPR; ch += kColThreads) {
+      const int rr = ch / CPR;
+      const int c = ch % CPR;
+      const int r = r0 + rr;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (r < R) {
+        const int tok = q0 + r % a.nq;
+        const int head = g * a.G + r / a.nq;
+        x = *(const uint4*)((const uint16_t*)a.q + ((long)tok * a.Hq + head) * D + c * 8);
+      }
+      *(uint4*)(sQ + rr * QS + c * 8) = x;
+    }
+    if (tid < 32) sL[tid] = (r0 + tid < R) ? lse2[r0 + tid] : INFINITY;
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+      const uint16_t* qr = sQ + col * QS + 8 * hi;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 qa = *(const bf16x8*)(qr + 16 * c);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][c], s, 0, 0, 0);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = (i >> 2) * 8 + hi * 4 + (i & 3);   // query row of accumulator i
+        part += __builtin_amdgcn_exp2f(s[i] * sl2 - sL[m]);
+      }
+      acc[kb] += (double)part;
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const double tot = acc[kb] + __shfl_xor(acc[kb], 32);
+    const int j = key0 + 32 * kb + col;
+    if (hi == 0 && j < a.L) scores[(long)hg * a.L + j] = (float)tot;
+  }
+}
+
+// float32 inputs: row statistics and column sums on the vector ALUs.
+template <int D>
+__global__ __launch_bounds__(256) void rowstat_f32_kernel(AttnArgs a) {
+  const int R = a.nq * a.G;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)a.V * a.Hkv * R) return;
+  const int r = (int)(gid % R);
+  const int hg = (int)(gid / R);
+  const int h = hg / a.Hkv, g = hg % a.Hkv;
+  const int tok = a.la + a.V * a.L + r % a.nq;
+  const int head = g * a.G + r / a.nq;
+  const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
+  float qv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) qv[c] = q[c];
+  const long kstr = (long)a.Hkv * D;
+  const float* kb = (const float*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
+  float m = -INFINITY, l = 0.0f;
+  for (int j = 0; j < a.L; ++j) {
+    const float* kr = kb + (long)j * kstr;
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) s = fmaf(qv[c], kr[c], s);
+    const float x = s * a.scale_log2;
+    const float mn = fmaxf(m, x);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
+    m = mn;
+  }
+  a.stats[gid] = m + __log2f(l);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __restrict__ scores) {
+  const int R = a.nq * a.G;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)a.V * a.Hkv * a.L) return;
+  const int j = (int)(gid % a.L);
+  const int hg = (int)(gid / a.L);
+  const int h = hg / a.Hkv, g = hg % a.Hkv;
+  const long kstr = (long)a.Hkv * D;
+  const float* kr = (const float*)a.k + (long)(a.la + h * a.L + j) * kstr + (long)g * D;
+  float kv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) kv[c] = kr[c];
+  const float* lse2 = a.stats + (long)hg * R;
+  double acc = 0.0;
+  for (int r = 0; r < R; ++r) {
+    const int tok = a.la + a.V * a.L + r % a.nq;
+    const int head = g * a.G + r / a.nq;
+    const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) s = fmaf(q[c], kv[c], s);
+    acc += (double)__builtin_amdgcn_exp2f(s * a.scale_log2 - lse2[r]);
+  }
+  scores[gid] = (float)acc;
+}
+
+__global__ void fill_zero_kernel(float* p, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Exact top-lp selection, one workgroup per (block, KV head) list.
+// ---------------------------------------------------------------------------
+constexpr int kTopkThreads = 1024;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup; returns this thread's prefix and
+// writes the total to *total.
+__device__ int block_exclusive_scan(int x, int* sWave, int* total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sWave[wave] = incl;
+  __syncthreads();
+  if (tid < 64) {
+    int w = (tid < kTopkThreads / 64) ? sWave[tid] : 0;
+    int wi = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(wi, o);
+      if (lane >= o) wi += y;
+    }
+    if (tid < kTopkThreads / 64) sWave[tid] = wi - w;   // exclusive wave offsets
+    if (tid == kTopkThreads / 64 - 1) sWave[kTopkThreads / 64] = wi;
+  }
+  __syncthreads();
+  const int res = sWave[wave] + incl - x;
+  *total = sWave[kTopkThreads / 64];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+                                                            int32_t* __restrict__ idx, int L, int lp) {
+  __shared__ int sHist[256];
+  __shared__ int sWave[kTopkThreads / 64 + 1];
+  __shared__ int sSel[2];
+  const int tid = threadIdx.x;
+  const float* sc = scores + (long)blockIdx.x * L;
+  int32_t* out = idx + (long)blockIdx.x * lp;
+
+  // Radix select of the lp-th largest order key, 8 bits at a time.
+  uint32_t prefix = 0, pmask = 0;
+  int need = lp;  // rank still to find among keys matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sHist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < L; j += kTopkThreads) {
+      const uint32_t u = order_key(sc[j]);
+      if ((u & pmask) == prefix) atomicAdd(&sHist[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    // Count of keys in digits above b (suffix sum from the top), by wave 0..3.
+    int cnt = 0, above = 0;
+    if (tid < 256) {
+      const int b = 255 - tid;           // tid 0 <-> digit 255
+      cnt = sHist[b];
+    }
+    // inclusive scan over tid (digits from the top) within the first 256 threads
+    int incl = cnt;
+    {
+      const int lane = tid & 63;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (tid < 256 && lane == 63) sWave[tid >> 6] = incl;
+      __syncthreads();
+      int off = 0;
+      for (int w = 0; w < (tid >> 6) && w < 4; ++w) off += sWave[w];
+      incl += off;
+      above = incl - cnt;
+    }
+    if (tid < 256 && above < need && need <= incl) {
+      sSel[0] = 255 - tid;
+      sSel[1] = need - above;
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)sSel[0];
+    need = sSel[1];
+    prefix |= digit << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // order key of the lp-th largest score
+  const int take_eq = need;     // keys equal to thr that are kept (lowest indices)
+
+  // Contiguous chunk per thread so the output comes out in index order.
+  const int chunk = (L + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = min(L, tid * chunk), j1 = min(L, j0 + chunk);
+  int n_eq = 0;
+  for (int j = j0; j < j1; ++j) n_eq += (order_key(sc[j]) == thr);
+  int eq_total;
+  int eq_before = block_exclusive_scan(n_eq, sWave, &eq_total);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = order_key(sc[j]);
+      if (u > thr) ++n_sel;
+      else if (u == thr) { if (e < take_eq) ++n_sel; ++e; }
+    }
+  }
+  int sel_total;
+  int pos = block_exclusive_scan(n_sel, sWave, &sel_total);
+  {
+    int e = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = order_key(sc[j]);
+      bool keep = false;
+      if (u > thr) keep = true;
+      else if (u == thr) { keep = e < take_eq; ++e; }
+      if (keep) out[pos++] = j;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s) {
+  const long nr = (long)a.V * a.Hkv * a.nq * a.G;
+  if (nr == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nr + 255) / 256));
+  if (a.D == 128)
+    hipLaunchKernelGGL((rowstat_f32_kernel<128>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((rowstat_f32_kernel<64>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Column sums; a.stats must already hold the row statistics.  With an empty
+// query block every score is 0 (a sum over no rows).
+hipError_t launch_colsum(const AttnArgs& a, float* scores, hipStream_t s) {
+  const long n = (long)a.V * a.Hkv * a.L;
+  if (n == 0) return hipSuccess;
+  if (a.nq * a.G == 0) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, scores, n);
+    return hipGetLastError();
+  }
+  if (a.f32) {
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (a.D == 128)
+      hipLaunchKernelGGL((colsum_f32_kernel<128>), grid, dim3(256), 0, s, a, scores);
+    else
+      hipLaunchKernelGGL((colsum_f32_kernel<64>), grid, dim3(256), 0, s, a, scores);
+  } else {
+    dim3 grid(ceil_div(a.L, kColKeys), a.V * a.Hkv);
+    if (a.D == 128)
+      hipLaunchKernelGGL((colsum_bf16_kernel<128>), grid, dim3(kColThreads), 0, s, a, scores);
+    else
+      hipLaunchKernelGGL((colsum_bf16_kernel<64>), grid, dim3(kColThreads), 0, s, a, scores);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s) {
+  if (n_lists == 0 || lp == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
+  return hipGetLastError();
+}
+
+}  // namespace spava

@@ -1,0 +1,263 @@
+// Internal declarations shared by the HIP translation units of libspava.
+//
+// Work decomposition of one layer (all virtual hosts on one GPU):
+//   * a "unit" is one workgroup's tile of query rows together with the list
+//     of key segments those rows attend to;
+//   * the kinds of unit follow the method's row types: anchor tokens,
+//     context tokens of host h, and the query block's partials (partial 0 =
+//     anchor + query block, partial h+1 = block h), plus a statistics-only
+//     pass over block h used by scoring.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spava.h"
+
+namespace spava {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKeyTile = 64;      // keys per attention tile; V^T segments pad to it
+constexpr int kRowsPerWave = 32;  // query rows per wave (MFMA 32x32 column block)
+
+enum UnitKind : int {
+  kAnchor = 0,    // anchor tokens, causal over the anchor
+  kContext = 1,   // context tokens of host h
+  kQueryHead = 2, // query partial 0: anchor + query block (causal)
+  kQueryBlock = 3,// query partial h+1: block h in full
+  kStats = 4,     // row log-sum-exp of the query rows over block h (no output O)
+};
+
+inline __host__ __device__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline __host__ __device__ int round_up(int a, int b) { return ceil_div(a, b) * b; }
+
+// Offsets of the padded, key-contiguous V copy ("V^T") kept in the attention
+// workspace: per KV head g and channel c, one row of keys laid out as
+//   [anchor | block 0 | ... | block V-1 | query], each padded to kKeyTile
+// with zeros, then the passing values [h=0..V-1][t] padded to kKeyTile.
+struct VtLayout {
+  int pad_anchor, pad_block, pad_query;  // padded segment lengths
+  int off_block0, off_query;             // offsets inside a main row
+  int main_len;                          // padded keys per main row
+  int pass_len;                          // padded passing keys per row
+  __host__ __device__ static VtLayout make(int la, int V, int L, int nq, int lp) {
+    VtLayout t;
+    t.pad_anchor = round_up(la, kKeyTile);
+    t.pad_block = round_up(L, kKeyTile);
+    t.pad_query = round_up(nq, kKeyTile);
+    t.off_block0 = t.pad_anchor;
+    t.off_query = t.pad_anchor + V * t.pad_block;
+    t.main_len = t.off_query + t.pad_query;
+    t.pass_len = round_up(V * lp, kKeyTile);
+    if (t.pass_len == 0) t.pass_len = kKeyTile;
+    return t;
+  }
+};
+
+// Everything an attention launch needs (passed by value as the kernel argument).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;       // row-major V (float32 path)
+  const void* kp;
+  const void* vp;      // row-major passing V (float32 path)
+  const uint16_t* vt;  // key-contiguous V (bf16 path)
+  const uint16_t* vpt; // key-contiguous passing V (bf16 path)
+  void* o;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  float* stats;        // kStats output: [V][Hkv][nq*G] log2-domain row LSE
+  int N, Hq, Hkv, G, D, la, V, L, nq, lp;
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  VtLayout vl;
+  // Unit ranges, in launch order (see unit_decode):
+  int n_ctx_units_per_host;  // ceil(L/BM) * Hq
+  int n_q_units;             // ceil(nq*G/BM) * Hkv, per query partial
+  int n_anchor_units;        // ceil(la/BM) * Hq
+  int rows_per_unit;         // BM
+  int stats_only;            // 1: launch covers kStats units only
+  int f32;                   // 1: float32 elements, 0: bf16
+};
+
+struct Unit {
+  int kind;
+  int host;      // kContext / kQueryBlock / kStats
+  int head;      // query head (single-head units)
+  int group;     // KV head
+  int tile;      // row tile index inside the unit's row space
+};
+
+// Launch order of units (longest rows first, roughly):
+//   context units of host V-1 down to 0 (later row tiles first),
+//   query-block partials of blocks 0..V-1, query partial 0, anchor units.
+// A stats launch covers V * n_q_units units, block-major.
+__device__ inline Unit unit_decode(const AttnArgs& a, int b) {
+  Unit u;
+  u.host = 0;
+  u.head = 0;
+  u.group = 0;
+  u.tile = 0;
+  const int bm = a.rows_per_unit;
+  if (a.stats_only) {
+    u.kind = kStats;
+    u.host = b / a.n_q_units;
+    int r = b % a.n_q_units;
+    u.group = r % a.Hkv;
+    u.tile = r / a.Hkv;
+    return u;
+  }
+  const int nctx = a.V * a.n_ctx_units_per_host;
+  if (b < nctx) {
+    u.kind = kContext;
+    u.host = a.V - 1 - b / a.n_ctx_units_per_host;
+    int r = b % a.n_ctx_units_per_host;
+    int ntile = ceil_div(a.L, bm);
+    u.head = r % a.Hq;
+    u.tile = ntile - 1 - r / a.Hq;
+    u.group = u.head / a.G;
+    return u;
+  }
+  b -= nctx;
+  const int nqb = a.V * a.n_q_units;
+  if (b < nqb) {
+    u.kind = kQueryBlock;
+    u.host = b / a.n_q_units;
+    int r = b % a.n_q_units;
+    u.group = r % a.Hkv;
+    u.tile = r / a.Hkv;
+    return u;
+  }
+  b -= nqb;
+  if (b < a.n_q_units) {
+    u.kind = kQueryHead;
+    u.group = b % a.Hkv;
+    u.tile = b / a.Hkv;
+    return u;
+  }
+  b -= a.n_q_units;
+  u.kind = kAnchor;
+  int ntile = ceil_div(a.la, bm);
+  u.head = b % a.Hq;
+  u.tile = ntile - 1 - b / a.Hq;
+  u.group = u.head / a.G;
+  return u;
+}
+
+__host__ inline int attn_total_units(const AttnArgs& a) {
+  if (a.stats_only) return a.V * a.n_q_units;
+  return a.V * a.n_ctx_units_per_host + a.V * a.n_q_units + a.n_q_units + a.n_anchor_units;
+}
+
+// A run of keys that a unit's rows attend to.
+struct Seg {
+  int kind;        // 0: rows of k (token-major, stride Hkv*D); 1: rows of kp
+  long k_off;      // element offset of key 0 of the segment in k or kp
+  long k_stride;   // elements between consecutive keys
+  long vt_off;     // element offset of key 0 in the V^T row of channel 0 (bf16 path)
+  int vt_pass;     // 1: segment lives in the passing V^T rows
+  long v_off;      // element offset of key 0 in v or vp (float32 path)
+  long v_stride;
+  int len;         // number of keys
+  int causal;      // 1: key token (tok0 + j) must be <= query token
+  int tok0;
+};
+
+// Key segments of a unit (at most 3).  Returns the count.
+__device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
+  const int g = u.group;
+  const long kstr = (long)a.Hkv * a.D;
+  int n = 0;
+  auto main_seg = [&](int tok0, int len, int vt_key_off, int causal) {
+    Seg x;
+    x.kind = 0;
+    x.k_off = (long)tok0 * kstr + (long)g * a.D;
+    x.k_stride = kstr;
+    x.vt_off = (long)g * a.D * a.vl.main_len + vt_key_off;
+    x.vt_pass = 0;
+    x.v_off = x.k_off;
+    x.v_stride = kstr;
+    x.len = len;
+    x.causal = causal;
+    x.tok0 = tok0;
+    s[n++] = x;
+  };
+  switch (u.kind) {
+    case kAnchor:
+      main_seg(0, a.la, 0, 1);
+      break;
+    case kContext: {
+      if (a.la > 0) main_seg(0, a.la, 0, 0);
+      if (u.host > 0 && a.lp > 0) {
+        Seg x;
+        x.kind = 1;
+        x.k_off = (long)g * a.V * a.lp * a.D;
+        x.k_stride = a.D;
+        x.vt_off = (long)g * a.D * a.vl.pass_len;
+        x.vt_pass = 1;
+        x.v_off = x.k_off;
+        x.v_stride = a.D;
+        x.len = u.host * a.lp;
+        x.causal = 0;
+        x.tok0 = 0;
+        s[n++] = x;
+      }
+      const int b0 = a.la + u.host * a.L;
+      main_seg(b0, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 1);
+      break;
+    }
+    case kQueryHead: {
+      if (a.la > 0) main_seg(0, a.la, 0, 0);
+      main_seg(a.la + a.V * a.L, a.nq, a.vl.off_query, 1);
+      break;
+    }
+    case kQueryBlock:
+    case kStats:
+      main_seg(a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
+      break;
+  }
+  return n;
+}
+
+// Row r of a unit's row space -> (token, query head, valid).
+// Single-head units: rows are consecutive tokens of one head.
+// Query units pack the G heads of a KV group: r = (a - g*G) * nq + i.
+struct RowId {
+  int tok, head, valid;
+};
+__device__ inline RowId unit_row(const AttnArgs& a, const Unit& u, int r) {
+  RowId x;
+  if (u.kind == kAnchor || u.kind == kContext) {
+    const int base = (u.kind == kAnchor) ? 0 : a.la + u.host * a.L;
+    const int n = (u.kind == kAnchor) ? a.la : a.L;
+    x.valid = r < n;
+    x.tok = base + (x.valid ? r : n - 1);
+    x.head = u.head;
+  } else {
+    const int R = a.nq * a.G;
+    x.valid = r < R;
+    const int rr = x.valid ? r : R - 1;
+    x.tok = a.la + a.V * a.L + rr % a.nq;
+    x.head = u.group * a.G + rr / a.nq;
+  }
+  return x;
+}
+
+// ---- launchers (host), defined in the .hip files ----
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s);
+hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_colsum(const AttnArgs& a, float* scores, hipStream_t s);
+hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);
+hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
+                         int la, int V, int L, int Hkv, int lp, int row_bytes, hipStream_t s);
+hipError_t launch_merge(int P, int R, int H, int D, const float* o_part, const float* lse_part,
+                        void* o, long o_row_stride, float* lse, long lse_head_stride,
+                        int out_bf16, hipStream_t s);
+
+}  // namespace spava

@@ -1,0 +1,96 @@
+"""The C-ABI library: it loads, exports every function include/spava.h
+declares, and rejects bad arguments on the host (no GPU needed: every call
+here fails validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_approximate_attention_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spava.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spava_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = S.lib()
+    names = declared_functions()
+    assert set(names) == set(S.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_empty_error():
+    assert S.lib().spava_version() == 100
+    assert isinstance(S.lib().spava_last_error(), bytes)
+
+
+def plan(**kw):
+    base = dict(n_anchor=32, n_hosts=4, host_len=128, n_query=16, n_q_heads=2, n_kv_heads=1,
+                head_dim=64, lp=16, dtype=S.SPAVA_F32, scale=0.0)
+    base.update(kw)
+    return S.Plan(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), S.SPAVA_OK),
+    (dict(lp=129), S.SPAVA_EINVAL),
+    (dict(lp=-1), S.SPAVA_EINVAL),
+    (dict(n_q_heads=3, n_kv_heads=2), S.SPAVA_EINVAL),
+    (dict(head_dim=96), S.SPAVA_EUNSUPPORTED),
+    (dict(dtype=7), S.SPAVA_EUNSUPPORTED),
+    (dict(n_hosts=0), S.SPAVA_EINVAL),
+    (dict(host_len=0), S.SPAVA_EINVAL),
+    (dict(n_query=-1), S.SPAVA_EINVAL),
+    (dict(scale=-1.0), S.SPAVA_EINVAL),
+    (dict(scale=float("nan")), S.SPAVA_EINVAL),
+    (dict(n_hosts=1, host_len=1 << 24, n_q_heads=64, n_kv_heads=8, head_dim=128, lp=0), S.SPAVA_EINVAL),
+    (dict(lp=0, n_query=0, n_anchor=0), S.SPAVA_OK),
+])
+def test_plan_check(kw, code):
+    assert S.spava_plan_check(plan(**kw)) == code
+    if code:
+        assert len(S.lib().spava_last_error()) > 0
+
+
+def test_workspace_sizes():
+    p = plan(dtype=S.SPAVA_BF16, head_dim=128)
+    # row statistics: V * Hkv * n_q * G floats
+    assert S.spava_score_topk_ws_bytes(p) == 4 * 1 * 16 * 2 * 4
+    # key-contiguous V: Hkv * d * (pad(la) + V*pad(L) + pad(n_q)) + passing, bf16
+    main = 1 * 128 * (64 + 4 * 128 + 64) * 2
+    pas = 1 * 128 * 64 * 2
+    assert S.spava_attn_fwd_ws_bytes(p) == main + pas
+    assert S.spava_attn_fwd_ws_bytes(plan(lp=999)) == 0
+
+
+def test_null_and_misaligned_pointers_rejected_on_host():
+    lib = S.lib()
+    p = plan().c()
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10004)
+    assert lib.spava_score_topk(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert lib.spava_score_topk(ctypes.byref(p), odd, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert lib.spava_score_topk(ctypes.byref(p), fake, fake, fake, fake, fake, 4, None) == S.SPAVA_EWORKSPACE
+    assert lib.spava_gather_passing(ctypes.byref(p), fake, None, fake, fake, fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                              fake, 1 << 20, None) == S.SPAVA_EINVAL
+    pb = plan(dtype=S.SPAVA_BF16).c()
+    assert lib.spava_attn_fwd(ctypes.byref(pb), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                              fake, 16, None) == S.SPAVA_EWORKSPACE
+    assert b"workspace" in lib.spava_last_error()
+    assert lib.spava_lse_merge(0, 4, 2, 64, fake, fake, fake, 128, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
+    assert lib.spava_lse_merge(2, 4, 2, 62, fake, fake, fake, 128, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
+    assert lib.spava_lse_merge(2, 4, 2, 64, fake, fake, fake, 64, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
+    assert lib.spava_lse_merge(2, 4, 2, 64, fake, fake, fake, 128, fake, 4, 9, None) == S.SPAVA_EUNSUPPORTED
+    # Nothing to do: succeeds without touching memory.
+    assert lib.spava_lse_merge(2, 0, 2, 64, None, None, None, 128, None, 0, S.SPAVA_F32, None) == S.SPAVA_OK
+    p0 = plan(lp=0).c()
+    assert lib.spava_gather_passing(ctypes.byref(p0), None, None, None, None, None, None) == S.SPAVA_OK
