@@ -82,6 +82,7 @@ struct AttnArgs {
   int rows_per_unit;         // BM
   int stats_only;            // 1: launch covers kStats units only
   int f32;                   // 1: float32 elements, 0: bf16
+  int xcd_chunk;             // units per XCD chunk (see xcd_unit)
 };
 
 struct Unit {
@@ -93,8 +94,9 @@ struct Unit {
 };
 
 // Launch order of units (longest rows first, roughly):
-//   context units of host V-1 down to 0 (later row tiles first),
+//   context units of host V-1 down to 0 (later row tiles first, heads fastest),
 //   query-block partials of blocks 0..V-1, query partial 0, anchor units.
+// Query-row units are KV-group-major so that units sharing K/V are adjacent.
 // A stats launch covers V * n_q_units units, block-major.
 __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   Unit u;
@@ -103,12 +105,13 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   u.group = 0;
   u.tile = 0;
   const int bm = a.rows_per_unit;
+  const int qt = a.n_q_units / a.Hkv;  // query row tiles per KV group
   if (a.stats_only) {
     u.kind = kStats;
     u.host = b / a.n_q_units;
     int r = b % a.n_q_units;
-    u.group = r % a.Hkv;
-    u.tile = r / a.Hkv;
+    u.group = r / qt;
+    u.tile = r % qt;
     return u;
   }
   const int nctx = a.V * a.n_ctx_units_per_host;
@@ -128,15 +131,15 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
     u.kind = kQueryBlock;
     u.host = b / a.n_q_units;
     int r = b % a.n_q_units;
-    u.group = r % a.Hkv;
-    u.tile = r / a.Hkv;
+    u.group = r / qt;
+    u.tile = r % qt;
     return u;
   }
   b -= nqb;
   if (b < a.n_q_units) {
     u.kind = kQueryHead;
-    u.group = b % a.Hkv;
-    u.tile = b / a.Hkv;
+    u.group = b / qt;
+    u.tile = b % qt;
     return u;
   }
   b -= a.n_q_units;
@@ -148,9 +151,24 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   return u;
 }
 
-__host__ inline int attn_total_units(const AttnArgs& a) {
+__host__ __device__ inline int attn_total_units(const AttnArgs& a) {
   if (a.stats_only) return a.V * a.n_q_units;
   return a.V * a.n_ctx_units_per_host + a.V * a.n_q_units + a.n_q_units + a.n_anchor_units;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8), and each XCD has its own L2.  Units are therefore dealt to XCDs in
+// chunks of `chunk` consecutive units (units that read the same K/V tiles),
+// keeping the launch order within each XCD.  The grid is padded to a
+// multiple of 8 * chunk; padding workgroups map past the last unit.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_grid(int n_units, int chunk) {
+  return round_up(n_units, kXcds * chunk);
+}
+__device__ inline int xcd_unit(int b, int chunk) {
+  const int x = b % kXcds;
+  const int s = b / kXcds;
+  return ((s / chunk) * kXcds + x) * chunk + s % chunk;
 }
 
 // A run of keys that a unit's rows attend to.
