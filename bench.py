@@ -49,6 +49,29 @@ def score_flops(w) -> float:
     return 2.0 * w.head_dim * (w.n_query * w.n_q_heads) * (w.n_hosts * w.host_len)
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_qwen3b_32k_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "sequence_approximate_attention_amd", "csrc", "attn_bf16.hip")
+
+
+def measured_traffic():
+    """HBM-side bytes per attention launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was
+    taken on a different kernel source than the one built here."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(TRAFFIC_SUMMARY):
+            if " = " in line:
+                key, val = line.strip().split(" = ", 1)
+                fields[key] = val
+        src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256") != src:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, x):
     """The oracle as it stands, on a bounded sample of the same layer:
     scoring + selection in full, then the context rows of hosts 0 and V-1
@@ -93,6 +116,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a reference "
+                         "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -132,6 +158,13 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -173,7 +206,8 @@ def main():
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "anchor": wl.n_anchor,
                    "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic()},
         "attn_tflop_per_launch": F_attn / 1e12,
         "step_tflops": (F_attn + score_flops(wl)) / (ms_per_step * 1e-3) / 1e12,
         "stage_ms": stage_ms,

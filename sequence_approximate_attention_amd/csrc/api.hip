@@ -9,7 +9,7 @@
 namespace spava {
 namespace {
 
-constexpr int kRowsPerUnit = 128;  // query rows per attention workgroup (both paths)
+constexpr int kRowsPerUnitF32 = 128;  // query rows per workgroup of the float32 kernel
 
 thread_local char g_err[512] = "";
 
@@ -63,11 +63,12 @@ AttnArgs make_args(const spava_plan* p) {
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)a.D);
   a.scale_log2 = a.scale * 1.44269504088896340736f;
   a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
-  a.rows_per_unit = kRowsPerUnit;
-  a.n_ctx_units_per_host = ceil_div(a.L, kRowsPerUnit) * a.Hq;
-  a.n_q_units = ceil_div(a.nq * a.G, kRowsPerUnit) * a.Hkv;
-  a.n_anchor_units = ceil_div(a.la, kRowsPerUnit) * a.Hq;
   a.f32 = p->dtype == SPAVA_F32;
+  const int bm = a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit();
+  a.rows_per_unit = bm;
+  a.n_ctx_units_per_host = ceil_div(a.L, bm) * a.Hq;
+  a.n_q_units = ceil_div(a.nq * a.G, bm) * a.Hkv;
+  a.n_anchor_units = ceil_div(a.la, bm) * a.Hq;
   return a;
 }
 

@@ -160,7 +160,15 @@ __device__ __forceinline__ SegRun sel(const SegRun& a0, const SegRun& a1, const 
   return r;
 }
 
+// Raw buffer descriptor (gfx9 family: word 3 = 0x00020000) over `bytes`
+// bytes from `base`; loads at offsets past the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // Issue this wave's share of the direct-to-LDS loads of tile t of run sr.
+// The K descriptor starts at the tile and ends at the segment's last key,
+// so rows past the segment read as zero (their logits are masked).
 template <int D, bool STATS>
 __device__ __forceinline__ void issue_tile(const SegRun& sr, int t, char* __restrict__ kbuf,
                                            char* __restrict__ vbuf, int wave, int lane) {
@@ -169,25 +177,26 @@ __device__ __forceinline__ void issue_tile(const SegRun& sr, int t, char* __rest
   constexpr int KRPI = 1024 / KRB;   // K rows per load instruction
   constexpr int KCPR = KRB / 16;     // 16-byte chunks per K row
   const int kb0 = t * kBN;
-  const uint16_t* kbase = sr.k + (long)kb0 * sr.kstride;
-  const int last = sr.len - 1 - kb0;  // largest valid tile-local key
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(sr.k + (long)kb0 * sr.kstride, (unsigned)(sr.len - kb0) * sr.kstride * 2u);
 #pragma unroll
   for (int j = 0; j < G::KINST; ++j) {
     const int blk = wave * G::KINST + j;
     const int row = blk * KRPI + lane / KCPR;
     const int c = swz<KRB>(row, lane % KCPR);      // involution: slot <-> chunk
-    const uint16_t* src = kbase + (min(row, last) * sr.kstride + c * 8);
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kbuf + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + blk * 1024), 16,
+                                             (row * sr.kstride + c * 8) * 2, 0, 0, 0);
   }
   if (!STATS) {
-    const uint16_t* vbase = sr.vt + kb0;
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(sr.vt + kb0, (unsigned)((D - 1) * sr.vrow + kBN) * 2u);
 #pragma unroll
     for (int j = 0; j < G::VINST; ++j) {
       const int blk = wave * G::VINST + j;
       const int row = blk * 8 + lane / 8;
       const int c = swz<128>(row, lane % 8);
-      const uint16_t* src = vbase + (row * sr.vrow + c * 8);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(vbuf + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + blk * 1024), 16,
+                                               (row * sr.vrow + c * 8) * 2, 0, 0, 0);
     }
   }
 }
@@ -269,20 +278,19 @@ __device__ __forceinline__ void tile_step(
       sacc[h2][e] = p;
       psum += p;
     }
-  st.l += psum;
-  if (!STATS) {
+  st.l += psum;   // float32 row sums: the LSE output needs them to ~1e-6
+  if (STATS) return;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int h2 = kc >> 1;
-      const int base = 8 * (kc & 1);
-      bf16x8 pb;
+  for (int kc = 0; kc < 4; ++kc) {
+    const int h2 = kc >> 1;
+    const int base = 8 * (kc & 1);
+    bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[h2][base + e];
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[h2][base + e];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)(vcur + voff[kc] + db * 32 * 128);
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[db], 0, 0, 0);
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x8 vf = *(const bf16x8*)(vcur + voff[kc] + db * 32 * 128);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[db], 0, 0, 0);
     }
   }
 }
@@ -439,6 +447,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 }
 
 }  // namespace
+
+int attn_bf16_rows_per_unit() { return kBM; }
 
 hipError_t launch_attn_bf16(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
