@@ -14,12 +14,16 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspava.so")
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "score.hip", "aux.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "rowstat_bf16.hip", "attn_f32.hip", "score.hip", "aux.hip"]
 ARCH = os.environ.get("SPAVA_ARCH", "gfx950")
 
 # Packed-FP32 instructions are disabled for the device code: plain float math
 # only (the flag is a device-side target feature; the host pass ignores it).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags.  The attention kernel keeps every MFMA accumulator
+# in the architectural VGPRs: with no AGPR use, two waves per SIMD get the
+# whole 256-register budget as VGPRs instead of an even VGPR/AGPR split.
+SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -31,7 +35,7 @@ def hipcc() -> str:
 
 def _compile(src: str, obj: str, extra: list[str]) -> None:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
-           os.path.join(CSRC, src), "-o", obj, *DEVICE_FLAGS, *extra]
+           os.path.join(CSRC, src), "-o", obj, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -47,7 +47,9 @@ int check_plan(const spava_plan* p) {
   return SPAVA_OK;
 }
 
-AttnArgs make_args(const spava_plan* p) {
+// rows_per_unit: query rows per workgroup of the kernel the arguments are
+// for (0 = the attention kernel of the plan's dtype).
+AttnArgs make_args(const spava_plan* p, int rows_per_unit = 0) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.Hq = p->n_q_heads;
@@ -64,7 +66,8 @@ AttnArgs make_args(const spava_plan* p) {
   a.scale_log2 = a.scale * 1.44269504088896340736f;
   a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
   a.f32 = p->dtype == SPAVA_F32;
-  const int bm = a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit();
+  const int bm = rows_per_unit > 0 ? rows_per_unit
+                                   : (a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit());
   a.rows_per_unit = bm;
   a.n_ctx_units_per_host = ceil_div(a.L, bm) * a.Hq;
   a.n_q_units = ceil_div(a.nq * a.G, bm) * a.Hkv;
@@ -125,7 +128,7 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float
   if (ws_bytes < stats_bytes(plan))
     return fail(SPAVA_EWORKSPACE, "spava_score_topk: workspace %zu < %zu bytes", ws_bytes, stats_bytes(plan));
   hipStream_t s = (hipStream_t)stream;
-  AttnArgs a = make_args(plan);
+  AttnArgs a = make_args(plan, plan->dtype == SPAVA_F32 ? 0 : rowstat_bf16_rows_per_unit());
   a.q = q;
   a.k = k;
   a.stats = (float*)ws;
@@ -134,8 +137,7 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float
     if (a.f32) {
       e = launch_rowstat_f32(a, s);
     } else {
-      a.stats_only = 1;
-      e = launch_attn_bf16(a, s);
+      e = launch_rowstat_bf16(a, s);
     }
     if (e != hipSuccess) return launched(e, "row statistics");
   }

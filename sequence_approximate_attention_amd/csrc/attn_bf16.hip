@@ -1,43 +1,66 @@
 // Fused approximate-attention forward for bf16 inputs on gfx950 (CDNA4).
 //
-// One workgroup = 4 waves = one unit of 128 query rows (32 per wave); two
-// workgroups share a CU (<= 256 registers per lane), so one workgroup's
-// softmax overlaps the other's matrix work.  The unit's key segments
-// (anchor / passing blocks / own block / query block, see unit_segments) are
-// walked in 64-key tiles that global_load_lds_dwordx4 copies straight into
-// double-buffered LDS (one barrier per tile):
-//   K tile   [64 keys][D]   row-major, read as the MFMA A operand
-//   V^T tile [D][64 keys]   key-contiguous, read as the MFMA A operand
-// LDS rows are XOR-swizzled in 16-byte slots so that the 16 rows one
-// ds_read_b128 phase touches fall in distinct banks.
+// Work unit: 256 query rows, one workgroup of 8 waves = 4 SIMD pairs.  Pair
+// s owns rows [64s, 64s+64) as two 32-column MFMA blocks and splits the work
+// between its two waves, which share one SIMD:
+//   softmax wave (wave s):   S = K Q^T on the matrix cores, then the masks,
+//                            row maxima, exponentials and row sums;
+//   output wave (wave 4+s):  O += V P on the matrix cores, and the tile copies.
+// The softmax wave's vector work then issues while the output wave's MFMAs
+// occupy the matrix core (a single wave can only slip a few vector
+// instructions under its own MFMAs), and every K or V^T fragment read from
+// LDS still feeds two MFMAs (64 rows per wave).
 //
-// Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane
-// owns one query column: the softmax row statistics live in one lane pair
-// (l, l^32) and rescaling O^T is lane-uniform.  P^T leaves the accumulator
-// registers directly as the B operand of O^T += V^T P^T: the A-operand rows
-// of the K tile are read in a permuted order (bits 2 and 3 of the row index
-// swapped), which makes the S^T accumulator layout equal to the B-operand
-// layout with keys in natural order.
+// Iteration i (one workgroup barrier each):
+//   softmax wave:  S(i) = K(i) Q^T || P(i-1) = exp2(S(i-1) - m), written to
+//                  LDS with its rescale factor; row maxima of S(i)
+//   output wave:   copies of V(i-1) and K(i+2); O = O*alpha(i-2) + V(i-2) P(i-2)
+// LDS: a 3-slot K ring, a 2-slot V^T ring (filled by buffer_load_dwordx4 ...
+// lds straight from memory) and a double-buffered P exchange.
+//   K tile   [64 keys][D]   row-major, read as the MFMA A operand of S^T
+//   V^T tile [D][64 keys]   key-contiguous, read as the MFMA A operand of O^T
+//   P tile   [2][4][64 lanes][8 bf16]  already in the B-operand layout
+// K and V^T rows are XOR-swizzled in 16-byte slots (the 16 rows of one
+// ds_read_b128 phase land in distinct banks).  Tiles past the end of the walk
+// are copied from an empty range and fully masked.
 //
-// The running maximum is only moved (and O^T rescaled) when a row's maximum
-// grows by more than 2^8 in the exp2 domain; otherwise probabilities are
-// taken against the stale maximum (at most 256, exact in the final
-// normalisation since O and the row sum share the same reference).
-//
-// STATS = true: no V and no PV; each row's log2-domain log-sum-exp over the
-// block is written for the block scoring (Figure 5 caption of the Spava
-// page: Q_qr K^(h)T estimates KV importance).
+// Math: S^T = K Q^T puts one query column per lane, so a row's softmax
+// statistics live in one lane pair (l, l^32) of the softmax wave.  K-tile rows
+// are read in a permuted order (bits 2 and 3 of the row index swapped) so that
+// the S^T accumulators already have the B-operand layout of O^T += V^T P^T
+// with keys in natural order.  Probabilities are taken against a stale
+// running maximum as long as they stay within [0, 2^8] (exact after
+// normalisation, since O and the row sum share the reference); a lane's sum
+// over its keys of a tile bounds every term, so the common path needs no row
+// maxima.  When a tile breaks the bound, its row maxima become the reference,
+// the row sums are rescaled, the tile's probabilities are recomputed, and the
+// output wave rescales O just before adding them.
 #include "spava_common.h"
 
 namespace spava {
 namespace {
 
-constexpr int kBM = 128;   // rows per workgroup
-constexpr int kBN = kKeyTile;
-constexpr int kThreads = 256;
+constexpr int kPairs = 4;                   // SIMD pairs
+constexpr int kWaves = 2 * kPairs;          // softmax waves 0-3, output waves 4-7
+constexpr int kWaveRows = 64;               // two 32-column MFMA blocks
+constexpr int kBM = kPairs * kWaveRows;     // rows per workgroup (unit)
+constexpr int kBN = kKeyTile;               // keys per tile
+constexpr int kThreads = kWaves * 64;
+constexpr int kKSlots = 3;                  // K ring: K(t) in slot t % 3
+constexpr int kVSlots = 2;                  // V^T ring: V(t) in slot t % 2
+constexpr int kPBytes = 2 * 4 * 64 * 16;    // P tile of one pair (64 rows x 64 keys, bf16)
 constexpr float kGrowLog2 = 8.0f;
 
-typedef __attribute__((address_space(3))) void lds_void;
+template <int D>
+struct Geo {
+  static constexpr int NC = D / 16;                   // 16-wide d chunks (K steps of S)
+  static constexpr int NDB = D / 32;                  // 32-row d blocks of O^T
+  static constexpr int KRB = D * 2;                   // bytes per K row
+  static constexpr int KBYTES = kBN * KRB;            // K tile
+  static constexpr int VBYTES = D * kBN * 2;          // V^T tile (rows of 64 keys = 128 B)
+  static constexpr int KINST = KBYTES / 1024 / kPairs;   // copy instructions per output wave
+  static constexpr int VINST = VBYTES / 1024 / kPairs;
+};
 
 __device__ __forceinline__ int perm_row(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -61,19 +84,19 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ ((r >> 1) & 7);
 }
 
-template <int D>
-struct Geo {
-  static constexpr int KRB = D * 2;                  // bytes per K row
-  static constexpr int KBYTES = kBN * KRB;           // K tile
-  static constexpr int VBYTES = D * kBN * 2;         // V^T tile (rows of 64 keys = 128 B)
-  static constexpr int KINST = KBYTES / 1024 / 4;    // K load instructions per wave
-  static constexpr int VINST = VBYTES / 1024 / 4;
-};
 
-// The unit's key segments as scalar fields (selected by value, never by a
+// s_waitcnt immediate (gfx9 encoding) that waits until at most N
+// vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The unit's key runs as scalar fields (selected by value, never by a
 // dynamic index, so that they stay in scalar registers).
 struct SegRun {
-  const uint16_t* k;   // key 0 of the segment (K or passing K rows)
+  const uint16_t* k;   // key 0 of the run (K or passing K rows)
   const uint16_t* vt;  // key 0 in the V^T row of channel 0
   int kstride;         // elements between consecutive keys
   int vrow;            // elements between consecutive V^T channel rows
@@ -116,200 +139,514 @@ __device__ __forceinline__ SegRun main_run(const AttnArgs& a, int g, int tok0, i
 //   anchor unit:        [anchor causal]
 //   context unit (h):   [anchor] [passing blocks 0..h-1] [own block causal]
 //   query partial 0:    [anchor] [query block causal]
-//   query partial h+1 / statistics over block h: [block h]
-__device__ __forceinline__ void unit_runs(const AttnArgs& a, const Unit& u, SegRun* r) {
+//   query partial h+1:  [block h]
+__device__ __forceinline__ void unit_runs(const AttnArgs& a, const Unit& u, SegRun& r0, SegRun& r1,
+                                          SegRun& r2) {
   const int g = u.group;
-  r[0] = empty_run();
-  r[1] = empty_run();
-  r[2] = empty_run();
+  r0 = empty_run();
+  r1 = empty_run();
+  r2 = empty_run();
   switch (u.kind) {
     case kAnchor:
-      r[0] = main_run(a, g, 0, a.la, 0, 1);
+      r0 = main_run(a, g, 0, a.la, 0, 1);
       break;
     case kContext:
-      r[0] = main_run(a, g, 0, a.la, 0, 0);
+      r0 = main_run(a, g, 0, a.la, 0, 0);
       if (u.host > 0 && a.lp > 0) {
-        r[1].k = (const uint16_t*)a.kp + (long)g * a.V * a.lp * a.D;
-        r[1].vt = a.vpt + (long)g * a.D * a.vl.pass_len;
-        r[1].kstride = a.D;
-        r[1].vrow = a.vl.pass_len;
-        r[1].len = u.host * a.lp;
+        r1.k = (const uint16_t*)a.kp + (long)g * a.V * a.lp * a.D;
+        r1.vt = a.vpt + (long)g * a.D * a.vl.pass_len;
+        r1.kstride = a.D;
+        r1.vrow = a.vl.pass_len;
+        r1.len = u.host * a.lp;
       }
-      r[2] = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 1);
+      r2 = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 1);
       break;
     case kQueryHead:
-      r[0] = main_run(a, g, 0, a.la, 0, 0);
-      r[1] = main_run(a, g, a.la + a.V * a.L, a.nq, a.vl.off_query, 1);
+      r0 = main_run(a, g, 0, a.la, 0, 0);
+      r1 = main_run(a, g, a.la + a.V * a.L, a.nq, a.vl.off_query, 1);
       break;
-    default:  // kQueryBlock, kStats
-      r[0] = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
+    default:  // kQueryBlock
+      r0 = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
       break;
   }
 }
 
-__device__ __forceinline__ SegRun sel(const SegRun& a0, const SegRun& a1, const SegRun& a2, int i) {
+// Selection on values (never on field lvalues, which would turn into a
+// select of addresses and keep the runs in scratch memory).
+template <typename T>
+__device__ __forceinline__ T pick3(T x0, T x1, T x2, int i) {
+  return i == 0 ? x0 : (i == 1 ? x1 : x2);
+}
+__device__ __forceinline__ SegRun sel(SegRun a0, SegRun a1, SegRun a2, int i) {
   SegRun r;
-  r.k = i == 0 ? a0.k : (i == 1 ? a1.k : a2.k);
-  r.vt = i == 0 ? a0.vt : (i == 1 ? a1.vt : a2.vt);
-  r.kstride = i == 0 ? a0.kstride : (i == 1 ? a1.kstride : a2.kstride);
-  r.vrow = i == 0 ? a0.vrow : (i == 1 ? a1.vrow : a2.vrow);
-  r.len = i == 0 ? a0.len : (i == 1 ? a1.len : a2.len);
-  r.causal = i == 0 ? a0.causal : (i == 1 ? a1.causal : a2.causal);
-  r.tok0 = i == 0 ? a0.tok0 : (i == 1 ? a1.tok0 : a2.tok0);
-  r.nt = i == 0 ? a0.nt : (i == 1 ? a1.nt : a2.nt);
+  r.k = pick3(a0.k, a1.k, a2.k, i);
+  r.vt = pick3(a0.vt, a1.vt, a2.vt, i);
+  r.kstride = pick3(a0.kstride, a1.kstride, a2.kstride, i);
+  r.vrow = pick3(a0.vrow, a1.vrow, a2.vrow, i);
+  r.len = pick3(a0.len, a1.len, a2.len, i);
+  r.causal = pick3(a0.causal, a1.causal, a2.causal, i);
+  r.tok0 = pick3(a0.tok0, a1.tok0, a2.tok0, i);
+  r.nt = pick3(a0.nt, a1.nt, a2.nt, i);
   return r;
 }
 
-// Raw buffer descriptor (gfx9 family: word 3 = 0x00020000) over `bytes`
-// bytes from `base`; loads at offsets past the range return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+// Wave-uniform values made visibly uniform (scalar registers, no waterfall
+// loops around the buffer descriptors built from them).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const uint16_t* uni(const uint16_t* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (const uint16_t*)(((unsigned long long)hi << 32) | lo);
 }
 
-// Issue this wave's share of the direct-to-LDS loads of tile t of run sr.
-// The K descriptor starts at the tile and ends at the segment's last key,
-// so rows past the segment read as zero (their logits are masked).
-template <int D, bool STATS>
-__device__ __forceinline__ void issue_tile(const SegRun& sr, int t, char* __restrict__ kbuf,
-                                           char* __restrict__ vbuf, int wave, int lane) {
-  using G = Geo<D>;
-  constexpr int KRB = G::KRB;
-  constexpr int KRPI = 1024 / KRB;   // K rows per load instruction
-  constexpr int KCPR = KRB / 16;     // 16-byte chunks per K row
-  const int kb0 = t * kBN;
-  const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc(sr.k + (long)kb0 * sr.kstride, (unsigned)(sr.len - kb0) * sr.kstride * 2u);
-#pragma unroll
-  for (int j = 0; j < G::KINST; ++j) {
-    const int blk = wave * G::KINST + j;
-    const int row = blk * KRPI + lane / KCPR;
-    const int c = swz<KRB>(row, lane % KCPR);      // involution: slot <-> chunk
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + blk * 1024), 16,
-                                             (row * sr.kstride + c * 8) * 2, 0, 0, 0);
+struct Runs {
+  SegRun r0, r1, r2;
+  int T;   // tiles in the walk
+};
+
+// Tile i of the unit's walk -> its run and first key.  Past the end of the
+// walk the run is empty (len 0): its copies read nothing and every logit of
+// the tile is masked.
+struct TileRef {
+  SegRun run;
+  int kb0;
+};
+__device__ __forceinline__ TileRef tile_ref(const Runs& R, int i) {
+  const int n0 = R.r0.nt, n1 = R.r1.nt;
+  const int s = (i >= n0) + (i >= n0 + n1);
+  const int t = i - (s >= 1 ? n0 : 0) - (s >= 2 ? n1 : 0);
+  const bool live = i < R.T;
+  TileRef r;
+  r.run = sel(R.r0, R.r1, R.r2, s);
+  r.run.k = uni(r.run.k);
+  r.run.vt = uni(r.run.vt);
+  r.run.kstride = uni(r.run.kstride);
+  r.run.vrow = uni(r.run.vrow);
+  r.run.len = uni(live ? r.run.len : 0);
+  r.run.causal = uni(live ? r.run.causal : 0);
+  r.run.tok0 = uni(r.run.tok0);
+  r.kb0 = uni(live ? t * kBN : 0);
+  return r;
+}
+
+// Raw buffer descriptor (gfx9 family: stride 0, word 3 = 0x00020000) over
+// `bytes` bytes from `base`, as four scalar words; loads at offsets past the
+// range return zero without touching memory.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((unsigned)b);
+  r.y = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;
+  return r;
+}
+
+// One buffer_load_dwordx4 ... lds: every lane's 16 bytes at byte offset
+// soff + voff of the buffer land at lds + 16 * lane.  Written as inline
+// assembly so that the compiler keeps no wait bookkeeping of its own for these
+// copies: their completion is awaited explicitly (wait_vm) before the barrier
+// that publishes a ring slot.  M0 carries the LDS address; it needs one wait
+// state before the load.
+__device__ __forceinline__ void copy16_to_lds(const u32x4& rsrc, unsigned soff, unsigned voff,
+                                              unsigned lds) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
+
+// Per-lane parts of the copy addresses.  A copy instruction moves 1 KB: R
+// rows of the tile (R = 4 for 256-byte K rows, 8 for 128-byte K rows and for
+// V^T rows), lane l writing 16 bytes at LDS slot l % (16 / (R / 4)) of row
+// l / (64 / R).  The XOR swizzle of that row splits into a lane part and a
+// part set by the copy index j: the source chunk is lane_chunk ^ (4 * j')
+// with j' = j for 4-row copies and j & 1 for 8-row copies.
+struct LaneCopy {
+  int kq, kx16;   // K: row within the copy, lane chunk * 16
+  int vq, vx16;   // V^T: the same
+};
+template <int D>
+__device__ __forceinline__ LaneCopy lane_copy(int lane) {
+  LaneCopy c;
+  if constexpr (D == 128) {            // 4 rows of 16 chunks: chunk = slot ^ (row & 15)
+    c.kq = lane >> 4;
+    c.kx16 = ((lane & 15) ^ c.kq) << 4;
+  } else {                             // 8 rows of 8 chunks: chunk = slot ^ ((row >> 1) & 7)
+    c.kq = lane >> 3;
+    c.kx16 = ((lane & 7) ^ (lane >> 4)) << 4;
   }
-  if (!STATS) {
-    const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(sr.vt + kb0, (unsigned)((D - 1) * sr.vrow + kBN) * 2u);
+  c.vq = lane >> 3;
+  c.vx16 = ((lane & 7) ^ (lane >> 4)) << 4;
+  return c;
+}
+
+// A cursor walking one operand's tiles through the unit's runs, in scalar
+// registers: moving to the next tile is an add and a subtract, and the run
+// table is only consulted when a run ends.
+struct Cursor {
+  unsigned long long addr;  // K: first key row of the tile; V^T: its first key in channel row 0
+  int rem;                  // bytes the copy may read from addr (0: nothing)
+  int stride2;              // bytes between the rows a copy reads (K: keys; V^T: channels)
+  int left;                 // tiles left in the current run, this one included
+  int s;                    // current run; 3 = past the walk
+};
+
+// Enter run s (or the first later run that has tiles) at its first tile.
+template <int D, bool IS_K>
+__device__ __forceinline__ void cursor_enter(Cursor& c, const Runs& R, int s) {
+  while (s < 3 && pick3(R.r0.nt, R.r1.nt, R.r2.nt, s) == 0) ++s;
+  c.s = s;
+  if (s >= 3) {
+    c.rem = 0;
+    c.left = 1 << 30;
+    return;
+  }
+  const SegRun r = sel(R.r0, R.r1, R.r2, s);
+  c.left = uni(r.nt);
+  if (IS_K) {
+    c.addr = (unsigned long long)uni(r.k);
+    c.stride2 = uni(r.kstride) * 2;
+    c.rem = uni(r.len) * c.stride2;   // to the run's end: rows past it read as zero
+  } else {
+    c.addr = (unsigned long long)uni(r.vt);
+    c.stride2 = uni(r.vrow) * 2;
+    c.rem = (D - 1) * c.stride2 + kBN * 2;   // one zero-padded tile
+  }
+}
+
+template <int D, bool IS_K>
+__device__ __forceinline__ void cursor_next(Cursor& c, const Runs& R) {
+  if (c.left > 1) {
+    --c.left;
+    if (IS_K) {
+      c.addr += (unsigned long long)(kBN * c.stride2);
+      c.rem -= kBN * c.stride2;
+    } else {
+      c.addr += kBN * 2;
+    }
+  } else {
+    cursor_enter<D, IS_K>(c, R, c.s + 1);
+  }
+}
+
+__device__ __forceinline__ u32x4 cursor_rsrc(const Cursor& c) {
+  u32x4 r;
+  r.x = (unsigned)c.addr;
+  r.y = (unsigned)(c.addr >> 32) & 0xffffu;
+  r.z = (unsigned)c.rem;
+  r.w = 0x00020000u;
+  return r;
+}
+
+// Copy instruction j (of Geo::KINST) of this wave's share of the K tile at
+// the cursor; qoff = this lane's row within the copy * stride.
+template <int D>
+__device__ __forceinline__ void copy_k(const Cursor& c, int qoff, const LaneCopy& lc, int j,
+                                       const char* kbuf, int wave) {
+  using G = Geo<D>;
+  constexpr int R = 1024 / G::KRB;            // rows per copy
+  const int blk = wave * G::KINST + j;
+  const int jx = (R == 4 ? j : (j & 1)) * 64;
+  copy16_to_lds(cursor_rsrc(c), (unsigned)(blk * R * c.stride2), (unsigned)(qoff + (lc.kx16 ^ jx)),
+                (unsigned)(unsigned long long)(kbuf + blk * 1024));
+}
+
+// Copy instruction j (of Geo::VINST) of this wave's share of the V^T tile at
+// the cursor (8 channel rows of 64 keys per copy).
+template <int D>
+__device__ __forceinline__ void copy_v(const Cursor& c, int qoff, const LaneCopy& lc, int j,
+                                       const char* vbuf, int wave) {
+  using G = Geo<D>;
+  const int blk = wave * G::VINST + j;
+  copy16_to_lds(cursor_rsrc(c), (unsigned)(blk * 8 * c.stride2), (unsigned)(qoff + (lc.vx16 ^ ((j & 1) * 64))),
+                (unsigned)(unsigned long long)(vbuf + blk * 1024));
+}
+
+// The whole of this wave's share of one tile's copies at once (prologue).
+template <int D>
+__device__ __forceinline__ void issue_k(const Cursor& c, const LaneCopy& lc, char* kbuf, int wave) {
+  const int qoff = lc.kq * c.stride2;
 #pragma unroll
-    for (int j = 0; j < G::VINST; ++j) {
-      const int blk = wave * G::VINST + j;
-      const int row = blk * 8 + lane / 8;
-      const int c = swz<128>(row, lane % 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + blk * 1024), 16,
-                                               (row * sr.vrow + c * 8) * 2, 0, 0, 0);
+  for (int j = 0; j < Geo<D>::KINST; ++j) copy_k<D>(c, qoff, lc, j, kbuf, wave);
+}
+template <int D>
+__device__ __forceinline__ void issue_v(const Cursor& c, const LaneCopy& lc, char* vbuf, int wave) {
+  const int qoff = lc.vq * c.stride2;
+#pragma unroll
+  for (int j = 0; j < Geo<D>::VINST; ++j) copy_v<D>(c, qoff, lc, j, vbuf, wave);
+}
+
+// Scores of one tile per (query block, 32-key half), and the bf16
+// probabilities of one tile per (query block, 16-key chunk).
+struct Scores {
+  f32x16 s[2][2];
+};
+struct Probs {
+  bf16x8 p[2][4];
+};
+
+// Softmax wave: constants and running statistics of its 64 rows.
+template <int D>
+struct SoftCtx {
+  bf16x8 qf[2][D / 16];  // Q^T fragments (B operand) per query block
+  int koff[D / 16];      // LDS byte offsets of this lane's K fragments
+  int qtok[2];           // this lane's query token per block
+  float sl2;             // softmax scale * log2(e)
+  int lane, hi;
+};
+struct SoftState {
+  float m[2];       // running max per query block, exp2 domain (scaled logits)
+  float l[2];       // this lane's partial row sums (its 16 keys of every 32)
+};
+
+// LDS byte offset of P chunk (qb, kc) for a lane: the output wave reads the
+// softmax wave's B-operand registers back with the same lane mapping.
+__device__ __forceinline__ int p_off(int qb, int kc, int lane) { return ((qb * 4 + kc) * 64 + lane) * 16; }
+
+// Probabilities of S(i-1) against the running maxima, straight to LDS;
+// returns (per lane) whether any of them may exceed 2^8 (row sum above it, or
+// not finite) or the row has no reference yet.
+template <int D>
+__device__ __forceinline__ bool soft_probs(const Scores& sp, char* pwrite, const SoftCtx<D>& cx,
+                                           const SoftState& st, float (&acc)[2]) {
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float m_use = (st.m[qb] == -INFINITY) ? 0.0f : st.m[qb];
+    float a = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sp.s[qb][kc >> 1][8 * (kc & 1) + e], cx.sl2, -m_use));
+        a += p;
+        pb[e] = (__bf16)p;
+      }
+      *(bf16x8*)(pwrite + p_off(qb, kc, cx.lane)) = pb;
+    }
+    acc[qb] = a;
+    grow |= !(a <= 256.0f) || st.m[qb] == -INFINITY;
+  }
+  return grow;
+}
+
+// One softmax-wave iteration.  kread holds K(i); P(i-1) and the factor that
+// moves O from the previous maximum to the one P(i-1) is computed against go
+// to pwrite, awrite, fwrite.  MASK applies the visibility limits of S(i).
+//
+// The maximum is only looked at when the probabilities of a tile could leave
+// [0, 2^8]: a lane's sum of its 32 probabilities bounds each of them, so the
+// common path needs no row maxima at all.  Then (rarely) the row maxima of
+// S(i-1) move the reference, the row sums are rescaled, P(i-1) is recomputed
+// and written again, and the output wave rescales O before adding it.
+template <int D, bool MASK>
+__device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __restrict__ kread,
+                                          char* __restrict__ pwrite, float* __restrict__ awrite,
+                                          int* __restrict__ fwrite, const SoftCtx<D>& cx, SoftState& st,
+                                          const Scores& s_prev, Scores& s_new) {
+  using G = Geo<D>;
+  constexpr int NC = G::NC;
+  constexpr int KRB = G::KRB;
+  constexpr int NA = 2 * NC;   // K fragments (h2, c)
+  constexpr int RING = 4;
+  asm volatile("" : "+s"(i));
+  __syncthreads();
+  // Fragment n = (d chunk c, key half h2) with h2 fastest: the four
+  // accumulators (qb, h2) alternate, so no MFMA waits on the one before.
+  auto kfrag = [&](int n) {
+    return *(const bf16x8*)(kread + cx.koff[n / 2] + (n % 2) * 32 * KRB);
+  };
+  // S(i) = K(i) Q^T, fragments RING reads ahead of their MFMAs.
+  bf16x8 ring[RING];
+#pragma unroll
+  for (int n = 0; n < RING; ++n) ring[n] = kfrag(n);
+#pragma unroll
+  for (int n = 0; n < NA; ++n) {
+    const bf16x8 af = ring[n % RING];
+    if (n + RING < NA) ring[n % RING] = kfrag(n + RING);
+    const int h2 = n % 2, c = n / 2;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      s_new.s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          af, cx.qf[qb][c], c == 0 ? f32x16{} : s_new.s[qb][h2], 0, 0, 0);
+  }
+  // P(i-1) = exp2(S(i-1) * sl2 - m).
+  float acc[2];
+  const bool grow = soft_probs<D>(s_prev, pwrite, cx, st, acc);
+  int moved = 0;
+  float alpha[2] = {1.0f, 1.0f};
+  if (__any(grow)) {
+    moved = 1;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x = fmaxf(x, s_prev.s[qb][h2][e]);
+      const float mp = fmaxf(x, __shfl_xor(x, 32)) * cx.sl2;
+      const float m_new = fmaxf(st.m[qb], mp);
+      alpha[qb] = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m[qb] - m_new);
+      st.m[qb] = m_new;
+      st.l[qb] *= alpha[qb];
+    }
+    soft_probs<D>(s_prev, pwrite, cx, st, acc);
+  }
+  st.l[0] += acc[0];   // float32 row sums: the LSE output needs them to ~1e-6
+  st.l[1] += acc[1];
+  if (cx.hi == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) awrite[qb * 32 + (cx.lane & 31)] = alpha[qb];
+  }
+  if (cx.lane == 0) *fwrite = moved;
+
+  // Visibility of S(i): keys past the run's end, or in a causal run past the
+  // row's token, get -inf.
+  if (MASK) {
+    const TileRef tr = tile_ref(run, i);
+    const SegRun& sr = tr.run;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      int lim = sr.len - tr.kb0;            // tile-local key j is visible iff j < lim
+      if (sr.causal) lim = min(lim, cx.qtok[qb] - sr.tok0 - tr.kb0 + 1);
+      const int lim1 = lim - 1 - 8 * cx.hi;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = 32 * h2 + (e & 7) + 16 * (e >> 3);
+          if (lim1 < j) s_new.s[qb][h2][e] = -INFINITY;
+        }
     }
   }
+}
+
+// Output wave: constants of its 64 rows and its share of the tile copies.
+template <int D>
+struct OutCtx {
+  int voff[4];    // LDS byte offsets of this lane's V^T fragments
+  LaneCopy lc;    // per-lane parts of the tile copy addresses
+  int w;          // index among the output waves (its share of each copy)
+  int lane;
+};
+
+// One output-wave iteration: copies of V(i-1) (to vload; empty for i = 0)
+// and K(i+2) (to kload), then O = O * alpha(i-2) + V(i-2) P(i-2) from vread,
+// pread, aread, fread.  Once only the last K copies (K(i+1)) may still be in
+// flight, V(i-2) and K(i) have landed; the barrier publishes them.
+template <int D>
+__device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __restrict__ vread,
+                                         const char* __restrict__ pread, const float* __restrict__ aread,
+                                         const int* __restrict__ fread, char* __restrict__ kload,
+                                         char* __restrict__ vload, const OutCtx<D>& cx,
+                                         f32x16 (&o)[2][D / 32], Cursor& kc, Cursor& vc) {
+  using G = Geo<D>;
+  constexpr int NDB = G::NDB;
+  asm volatile("" : "+s"(i));
+  wait_vm<G::KINST>();
+  __syncthreads();
+  constexpr int NB = 4 * NDB;   // V^T fragments (kc, db)
+  constexpr int RING = 4;
+  if (i >= 2) {
+    // The rescale flag, P(i-2) and the first V^T fragments are all in
+    // flight before the flag is looked at.
+    const int moved = *fread;
+    auto vfrag = [&](int n) {
+      return *(const bf16x8*)(vread + cx.voff[n / NDB] + (n % NDB) * 32 * 128);
+    };
+    bf16x8 pf[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) pf[qb][ch] = *(const bf16x8*)(pread + p_off(qb, ch, cx.lane));
+    bf16x8 ring[RING];
+#pragma unroll
+    for (int n = 0; n < RING; ++n) ring[n] = vfrag(n);
+    if (__builtin_amdgcn_readfirstlane(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float alpha = aread[qb * 32 + (cx.lane & 31)];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+      }
+    }
+    // O += V(i-2) P(i-2) through the fragment ring; the tile copies go out
+    // after the first MFMAs.
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const bf16x8 vf = ring[n % RING];
+      if (n + RING < NB) ring[n % RING] = vfrag(n + RING);
+      const int ch = n / NDB, db = n % NDB;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ch], o[qb][db], 0, 0, 0);
+      if (n == 1) {
+        issue_v<D>(vc, cx.lc, vload, cx.w);
+        cursor_next<D, false>(vc, run);
+        issue_k<D>(kc, cx.lc, kload, cx.w);
+        cursor_next<D, true>(kc, run);
+      }
+    }
+  } else {
+    // Nothing to add yet; V(-1) is empty.
+    if (i == 0) {
+      Cursor none = vc;
+      none.rem = 0;
+      issue_v<D>(none, cx.lc, vload, cx.w);
+    } else {
+      issue_v<D>(vc, cx.lc, vload, cx.w);
+      cursor_next<D, false>(vc, run);
+    }
+    issue_k<D>(kc, cx.lc, kload, cx.w);
+    cursor_next<D, true>(kc, run);
+  }
+}
+
+// Leading tiles of the walk that no row of the workgroup sees partly: the
+// softmax waves run them without masks.  gmin is the workgroup's smallest
+// query token.
+__device__ __forceinline__ int unmasked_prefix(const Runs& R, int gmin) {
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const SegRun r = s == 0 ? R.r0 : (s == 1 ? R.r1 : R.r2);
+    int nf = r.len / kBN;                              // whole tiles of the run
+    if (r.causal) nf = min(nf, max(0, (gmin - r.tok0 + 1) / kBN));
+    nf = min(nf, r.nt);
+    if (nf < r.nt) return base + nf;
+    base += r.nt;
+  }
+  return base;
 }
 
 template <int D>
-struct RowState {
-  f32x16 o[D / 32];
-  float m;   // running max, exp2 domain (scaled logits)
-  float l;   // this lane's partial row sum (its 16 keys of every 32)
-};
-
-// One key tile: prefetch the next tile into the other buffers, then
-// S^T = K Q^T, mask, online softmax, O^T += V^T P^T from the current ones.
-// The buffers are distinct restrict pointers so that reads of the current
-// tile need not wait for the in-flight copies of the next one.
-template <int D, bool STATS>
-__device__ __forceinline__ void tile_step(
-    const char* __restrict__ kcur, const char* __restrict__ vcur, char* __restrict__ knext,
-    char* __restrict__ vnext, bool issue, const SegRun& nrun, int nt, const SegRun& cur, int ct,
-    const bf16x8* qf, const int* koff, const int* voff, RowState<D>& st, float sl2, int row_tok,
-    int wmin, int wmax, int wave, int lane, int hi) {
-  constexpr int NC = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int KRB = Geo<D>::KRB;
-  if (issue) issue_tile<D, STATS>(nrun, nt, knext, vnext, wave, lane);
-  const int kb0 = ct * kBN;
-  if (cur.causal && cur.tok0 + kb0 > wmax) return;   // every key is in this wave's future
-
-  f32x16 sacc[2];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bf16x8 af = *(const bf16x8*)(kcur + koff[c] + h2 * 32 * KRB);
-      sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], sacc[h2], 0, 0, 0);
-    }
-  }
-  const bool need_mask = (kb0 + kBN > cur.len) || (cur.causal && cur.tok0 + kb0 + kBN - 1 > wmin);
-  if (need_mask) {
-    // Tile-local key j is visible iff j < lim.
-    int lim = cur.len - kb0;
-    if (cur.causal) lim = min(lim, row_tok - cur.tok0 - kb0 + 1);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = 32 * h2 + (e & 7) + 8 * hi + 16 * (e >> 3);
-        if (j >= lim) sacc[h2][e] = -INFINITY;
-      }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-  const bool grow = mx > st.m + kGrowLog2;
-  if (__any(grow)) {
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // m = -inf -> 0
-    st.m = m_new;
-    st.l *= alpha;
-    if (!STATS) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
-    }
-  }
-  const float m_use = (st.m == -INFINITY) ? 0.0f : st.m;
-  float psum = 0.0f;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][e], sl2, -m_use));
-      sacc[h2][e] = p;
-      psum += p;
-    }
-  st.l += psum;   // float32 row sums: the LSE output needs them to ~1e-6
-  if (STATS) return;
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    const int h2 = kc >> 1;
-    const int base = 8 * (kc & 1);
-    bf16x8 pb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[h2][base + e];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16x8 vf = *(const bf16x8*)(vcur + voff[kc] + db * 32 * 128);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[db], 0, 0, 0);
-    }
-  }
-}
-
-template <int D, bool STATS>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   using G = Geo<D>;
-  constexpr int NC = D / 16;   // 16-wide d chunks (MFMA K steps of S)
-  constexpr int NDB = D / 32;  // 32-row d blocks of O^T
+  constexpr int NC = G::NC;
+  constexpr int NDB = G::NDB;
   constexpr int KRB = G::KRB;
-  __shared__ __attribute__((aligned(1024))) char sK0[G::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[G::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[STATS ? 16 : G::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[STATS ? 16 : G::VBYTES];
-  __shared__ int sTok[4];
+  __shared__ __attribute__((aligned(1024))) char sK[kKSlots * G::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[kVSlots * G::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sP[2 * kPairs * kPBytes];
+  __shared__ float sAlpha[2 * kPairs * 64];
+  __shared__ int sFlag[2 * kPairs];
+  __shared__ int sTok[2 * kWaves];
+  __shared__ float sL[kPairs * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (kPairs - 1);
+  const bool soft = wave < kPairs;
   const int hi = lane >> 5;
   const int col = lane & 31;
 
@@ -317,132 +654,201 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int b = xcd_unit(blockIdx.x, a.xcd_chunk);
   if (b >= n_units) return;
   const Unit u = unit_decode(a, b);
-  SegRun run[3];
-  unit_runs(a, u, run);
+  Runs run;
+  unit_runs(a, u, run.r0, run.r1, run.r2);
 
-  const int r = u.tile * kBM + wave * kRowsPerWave + col;
-  const RowId row = unit_row(a, u, r);
+  // This lane's query row in each of the pair's two 32-column blocks.
+  RowId row[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) row[qb] = unit_row(a, u, u.tile * kBM + pair * kWaveRows + 32 * qb + col);
 
-  // Q^T fragments (B operand): lane holds its query's d = 16c + 8*hi .. +7.
-  bf16x8 qf[NC];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + ((long)row.tok * a.Hq + row.head) * D + 8 * hi;
+  // Token range of the workgroup (tile count, mask-free prefix).
+  int tmin = 0x7fffffff, tmax = -1;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qf[c] = *(const bf16x8*)(qp + 16 * c);
-      if (!row.valid) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.0f;
-      }
+  for (int qb = 0; qb < 2; ++qb)
+    if (row[qb].valid) {
+      tmin = min(tmin, row[qb].tok);
+      tmax = max(tmax, row[qb].tok);
     }
+  tmin = wave_reduce_min(tmin);
+  tmax = wave_reduce_max(tmax);
+  if (lane == 0) {
+    sTok[wave] = tmax;
+    sTok[kWaves + wave] = tmin;
   }
-
-  // Token range of this wave (masking, skipping) and of the workgroup (tile count).
-  const int wmin = wave_reduce_min(row.valid ? row.tok : 0x7fffffff);
-  const int wmax = wave_reduce_max(row.valid ? row.tok : -1);
-  if (lane == 0) sTok[wave] = wmax;
   __syncthreads();
-  const int gmax = max(max(sTok[0], sTok[1]), max(sTok[2], sTok[3]));
-
+  int gmax = sTok[0], gmin = sTok[kWaves];
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    int n = run[s].len;
-    if (run[s].causal) n = min(n, gmax - run[s].tok0 + 1);
-    run[s].nt = n > 0 ? ceil_div(n, kBN) : 0;
+  for (int w = 1; w < kWaves; ++w) {
+    gmax = max(gmax, sTok[w]);
+    gmin = min(gmin, sTok[kWaves + w]);
   }
-  const int T = run[0].nt + run[1].nt + run[2].nt;
-
-  // Per-lane LDS byte offsets of the A-operand fragments.
-  const int krow = perm_row(col);                 // + 32 per 32-key half
-  int koff[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) koff[c] = krow * KRB + swz<KRB>(krow, 2 * c + hi) * 16;
-  int voff[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) voff[kc] = col * 128 + swz<128>(col, 2 * kc + hi) * 16;
-
-  RowState<D> st;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st.o[db][e] = 0.0f;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-  const float sl2 = a.scale_log2;
-
-  // Tile i -> (run, tile): runs are visited in order, skipping empty ones.
-  auto locate = [&](int i, int& s, int& t) {
-    const int n0 = run[0].nt, n1 = run[1].nt;
-    s = (i >= n0) + (i >= n0 + n1);
-    t = i - (s >= 1 ? n0 : 0) - (s >= 2 ? n1 : 0);
+  auto tiles = [&](SegRun& x) {
+    int n = x.len;
+    if (x.causal) n = min(n, gmax - x.tok0 + 1);
+    x.nt = uni(n > 0 ? ceil_div(n, kBN) : 0);
   };
-  if (T > 0) {
-    int s0, t0;
-    locate(0, s0, t0);
-    issue_tile<D, STATS>(sel(run[0], run[1], run[2], s0), t0, sK0, sV0, wave, lane);
-  }
-  for (int i = 0; i < T; i += 2) {
-    int s, t, sn, tn;
-    locate(i, s, t);
-    locate(i + 1, sn, tn);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    tile_step<D, STATS>(sK0, sV0, sK1, sV1, i + 1 < T, sel(run[0], run[1], run[2], sn), tn,
-                        sel(run[0], run[1], run[2], s), t, qf, koff, voff, st, sl2, row.tok, wmin,
-                        wmax, wave, lane, hi);
-    if (i + 1 >= T) break;
-    int s2, t2;
-    locate(i + 2, s2, t2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    tile_step<D, STATS>(sK1, sV1, sK0, sV0, i + 2 < T, sel(run[0], run[1], run[2], s2), t2,
-                        sel(run[0], run[1], run[2], sn), tn, qf, koff, voff, st, sl2, row.tok,
-                        wmin, wmax, wave, lane, hi);
-  }
+  tiles(run.r0);
+  tiles(run.r1);
+  tiles(run.r2);
+  run.T = run.r0.nt + run.r1.nt + run.r2.nt;
+  const int n_iter = run.T + 2;   // iteration T+1 adds the last P V
 
-  // Epilogue.
-  const float lt = st.l + __shfl_xor(st.l, 32);
-  const float lse2 = (lt > 0.0f) ? st.m + __log2f(lt) : -INFINITY;
-  if (STATS) {
-    if (hi == 0 && row.valid) {
-      const int R = a.nq * a.G;
-      a.stats[((long)u.host * a.Hkv + u.group) * R + r] = lse2;
+  if (soft) {
+    SoftCtx<D> cx;
+    cx.lane = lane;
+    cx.hi = hi;
+    cx.sl2 = a.scale_log2;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      cx.qtok[qb] = row[qb].tok;
+      const uint16_t* qp = (const uint16_t*)a.q + ((long)row[qb].tok * a.Hq + row[qb].head) * D + 8 * hi;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        cx.qf[qb][c] = *(const bf16x8*)(qp + 16 * c);
+        if (!row[qb].valid) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cx.qf[qb][c][e] = (__bf16)0.0f;
+        }
+      }
     }
-    return;
-  }
-  if (!row.valid) return;
-  const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
-  const float lse_nat = lse2 * 0.69314718055994530942f;
-  if (u.kind == kAnchor || u.kind == kContext) {
-    uint16_t* op = (uint16_t*)a.o + ((long)row.tok * a.Hq + row.head) * D;
+    const int krow = perm_row(col);               // + 32 per 32-key half
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int c = 0; c < NC; ++c) cx.koff[c] = krow * KRB + swz<KRB>(krow, 2 * c + hi) * 16;
+
+    SoftState st;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hi;
-        union { __bf16 h[4]; uint2 u; } pk;
+    for (int qb = 0; qb < 2; ++qb) {
+      st.m[qb] = -INFINITY;
+      st.l[qb] = 0.0f;
+    }
+    Scores sA, sB;   // S(-1) = -inf: no probabilities
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(st.o[db][4 * g4 + e] * inv);
-        *(uint2*)(op + d0) = pk.u;
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sA.s[qb][h2][e] = -INFINITY;
+
+    // Slots of iteration i: K(i) in i % 3; P(i-1) and its factor in buffer
+    // (i-1) % 2 (even and odd iterations are unrolled with fixed buffers).
+    int k3 = 0;   // i % 3
+    auto knext = [&]() {
+      const char* r = sK + k3 * G::KBYTES;
+      k3 = (k3 == kKSlots - 1) ? 0 : k3 + 1;
+      return r;
+    };
+    char* const p0 = sP + pair * kPBytes;
+    char* const p1 = sP + (kPairs + pair) * kPBytes;
+    float* const a0 = sAlpha + pair * 64;
+    float* const a1 = sAlpha + (kPairs + pair) * 64;
+    int* const f0 = sFlag + pair;
+    int* const f1 = sFlag + kPairs + pair;
+    const int n_plain = min(unmasked_prefix(run, gmin), n_iter) & ~1;
+    for (int i = 0; i < n_plain; i += 2) {
+      soft_iter<D, false>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, false>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    }
+    for (int i = n_plain; i < n_iter; i += 2) {
+      soft_iter<D, true>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      if (i + 1 >= n_iter) break;
+      soft_iter<D, true>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    }
+    // Row sums to the output wave; LSE out.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float lt = st.l[qb] + __shfl_xor(st.l[qb], 32);
+      if (hi == 0) sL[pair * 64 + qb * 32 + col] = lt;
+      if (hi != 0 || !row[qb].valid) continue;
+      const float lse_nat = (lt > 0.0f) ? (st.m[qb] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+      if (u.kind == kAnchor || u.kind == kContext) {
+        a.lse[(long)row[qb].head * a.N + row[qb].tok] = lse_nat;
+      } else {
+        const int p = (u.kind == kQueryHead) ? 0 : u.host + 1;
+        const int qi = row[qb].tok - (a.la + a.V * a.L);
+        a.lse_part[((long)p * a.Hq + row[qb].head) * a.nq + qi] = lse_nat;
       }
-    if (hi == 0) a.lse[(long)row.head * a.N + row.tok] = lse_nat;
+    }
+    __syncthreads();
   } else {
-    const int p = (u.kind == kQueryHead) ? 0 : u.host + 1;
-    const int i = row.tok - (a.la + a.V * a.L);
-    float* op = a.o_part + (((long)p * a.nq + i) * a.Hq + row.head) * D;
+    OutCtx<D> cx;
+    cx.lane = lane;
+    cx.w = wave - kPairs;
+    cx.lc = lane_copy<D>(lane);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kc = 0; kc < 4; ++kc) cx.voff[kc] = col * 128 + swz<128>(col, 2 * kc + hi) * 16;
+    f32x16 o[2][NDB];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hi;
-        float4 w;
-        w.x = st.o[db][4 * g4 + 0] * inv;
-        w.y = st.o[db][4 * g4 + 1] * inv;
-        w.z = st.o[db][4 * g4 + 2] * inv;
-        w.w = st.o[db][4 * g4 + 3] * inv;
-        *(float4*)(op + d0) = w;
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.0f;
+
+    // K(0) and K(1) ahead of iteration 0; the cursors then stand at K(2) and V(0).
+    Cursor kc, vc;
+    cursor_enter<D, true>(kc, run, 0);
+    cursor_enter<D, false>(vc, run, 0);
+    issue_k<D>(kc, cx.lc, sK, cx.w);
+    cursor_next<D, true>(kc, run);
+    issue_k<D>(kc, cx.lc, sK + G::KBYTES, cx.w);
+    cursor_next<D, true>(kc, run);
+
+    // Iteration i: copies of V(i-1) into slot (i+1) % 2 and of K(i+2) into
+    // slot (i+2) % 3; reads V(i-2) from slot i % 2 and P(i-2) from buffer i % 2.
+    int k3 = 2;   // (i + 2) % 3
+    char* const v0 = sV;
+    char* const v1 = sV + G::VBYTES;
+    const char* const p0 = sP + pair * kPBytes;
+    const char* const p1 = sP + (kPairs + pair) * kPBytes;
+    const float* const a0 = sAlpha + pair * 64;
+    const float* const a1 = sAlpha + (kPairs + pair) * 64;
+    const int* const f0 = sFlag + pair;
+    const int* const f1 = sFlag + kPairs + pair;
+    for (int i = 0; i < n_iter; i += 2) {
+      out_iter<D>(i, run, v0, p0, a0, f0, sK + k3 * G::KBYTES, v1, cx, o, kc, vc);
+      k3 = (k3 == kKSlots - 1) ? 0 : k3 + 1;
+      if (i + 1 >= n_iter) break;
+      out_iter<D>(i + 1, run, v1, p1, a1, f1, sK + k3 * G::KBYTES, v0, cx, o, kc, vc);
+      k3 = (k3 == kKSlots - 1) ? 0 : k3 + 1;
+    }
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (!row[qb].valid) continue;
+      const float lt = sL[pair * 64 + qb * 32 + col];
+      const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+      if (u.kind == kAnchor || u.kind == kContext) {
+        uint16_t* op = (uint16_t*)a.o + ((long)row[qb].tok * a.Hq + row[qb].head) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hi;
+            union { __bf16 h[4]; uint2 u; } pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(o[qb][db][4 * g4 + e] * inv);
+            *(uint2*)(op + d0) = pk.u;
+          }
+      } else {
+        const int p = (u.kind == kQueryHead) ? 0 : u.host + 1;
+        const int qi = row[qb].tok - (a.la + a.V * a.L);
+        float* op = a.o_part + (((long)p * a.nq + qi) * a.Hq + row[qb].head) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * db + 8 * g4 + 4 * hi;
+            float4 w;
+            w.x = o[qb][db][4 * g4 + 0] * inv;
+            w.y = o[qb][db][4 * g4 + 1] * inv;
+            w.z = o[qb][db][4 * g4 + 2] * inv;
+            w.w = o[qb][db][4 * g4 + 3] * inv;
+            *(float4*)(op + d0) = w;
+          }
       }
-    if (hi == 0) a.lse_part[((long)p * a.Hq + row.head) * a.nq + i] = lse_nat;
+    }
   }
 }
 
@@ -454,19 +860,12 @@ hipError_t launch_attn_bf16(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
   const int n = attn_total_units(a);
   if (n == 0) return hipSuccess;
-  a.xcd_chunk = a.stats_only ? max(1, a.n_q_units / a.Hkv) : a.Hq;
+  a.xcd_chunk = a.Hq;
   const dim3 grid(xcd_grid(n, a.xcd_chunk));
-  if (a.D == 128) {
-    if (a.stats_only)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
-  } else {
-    if (a.stats_only)
-      hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
-  }
+  if (a.D == 128)
+    hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<64>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -268,6 +268,8 @@ __device__ inline RowId unit_row(const AttnArgs& a, const Unit& u, int r) {
 // ---- launchers (host), defined in the .hip files ----
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
+hipError_t launch_rowstat_bf16(const AttnArgs& a, hipStream_t s);   // kStats units
+int rowstat_bf16_rows_per_unit();
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s);
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
