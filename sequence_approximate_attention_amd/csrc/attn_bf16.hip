@@ -463,7 +463,17 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   auto kfrag = [&](int n) {
     return *(const bf16x8*)(kread + cx.koff[n / 2] + (n % 2) * 32 * KRB);
   };
-  // S(i) = K(i) Q^T, fragments RING reads ahead of their MFMAs.
+  // S(i) = K(i) Q^T, fragments RING reads ahead of their MFMAs, with the
+  // probabilities P(i-1) = exp2(S(i-1) * sl2 - m) computed in even chunks
+  // between the MFMA pairs: the softmax wave's vector work then issues while
+  // the matrix core runs this wave's or the output wave's MFMAs, instead of
+  // after all of them.
+  constexpr int PPC = 64 / NA;   // probabilities per fragment step
+  float mu[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) mu[qb] = (st.m[qb] == -INFINITY) ? 0.0f : st.m[qb];
+  float acc[2] = {0.0f, 0.0f};
+  bf16x8 pb;
   bf16x8 ring[RING];
 #pragma unroll
   for (int n = 0; n < RING; ++n) ring[n] = kfrag(n);
@@ -476,17 +486,27 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
     for (int qb = 0; qb < 2; ++qb)
       s_new.s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           af, cx.qf[qb][c], c == 0 ? f32x16{} : s_new.s[qb][h2], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < PPC; ++t) {
+      const int idx = n * PPC + t;
+      const int qb = idx >> 5, kc = (idx >> 3) & 3, e = idx & 7;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s_prev.s[qb][kc >> 1][8 * (kc & 1) + e], cx.sl2, -mu[qb]));
+      acc[qb] += p;
+      pb[e] = (__bf16)p;
+      if (e == 7) *(bf16x8*)(pwrite + p_off(qb, kc, cx.lane)) = pb;
+    }
   }
-  // P(i-1) = exp2(S(i-1) * sl2 - m).
-  float acc[2];
-  const bool grow = soft_probs<D>(s_prev, pwrite, cx, st, acc);
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) grow |= !(acc[qb] <= 256.0f) || st.m[qb] == -INFINITY;
   int moved = 0;
   float alpha[2] = {1.0f, 1.0f};
   if (__any(grow)) {
     moved = 1;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float x = -INFINITY;
+      float x;
+      asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(x));   // -inf, computed only here
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -579,8 +599,7 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
           for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
       }
     }
-    // O += V(i-2) P(i-2) through the fragment ring; the tile copies go out
-    // after the first MFMAs.
+    // O += V(i-2) P(i-2) through the fragment ring.
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const bf16x8 vf = ring[n % RING];
@@ -589,12 +608,12 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ch], o[qb][db], 0, 0, 0);
-      if (n == 1) {
-        issue_v<D>(vc, cx.lc, vload, cx.w);
-        cursor_next<D, false>(vc, run);
-        issue_k<D>(kc, cx.lc, kload, cx.w);
-        cursor_next<D, true>(kc, run);
-      }
+      // The tile copies go out one per MFMA pair: V(i-1), then K(i+2).
+      if (n >= 1 && n < 1 + G::VINST) copy_v<D>(vc, cx.lc.vq * vc.stride2, cx.lc, n - 1, vload, cx.w);
+      if (n == G::VINST) cursor_next<D, false>(vc, run);
+      if (n >= 1 + G::VINST && n < 1 + G::VINST + G::KINST)
+        copy_k<D>(kc, cx.lc.kq * kc.stride2, cx.lc, n - 1 - G::VINST, kload, cx.w);
+      if (n == G::VINST + G::KINST) cursor_next<D, true>(kc, run);
     }
   } else {
     // Nothing to add yet; V(-1) is empty.
