@@ -95,8 +95,12 @@ const char* spava_last_error(void);
 int spava_plan_check(const spava_plan* plan);
 
 /*
- * Workspace bytes spava_score_topk needs: the per-row log-sum-exp of the
- * query rows over each block, float32 [V][Hkv][n_q*G], rounded up.
+ * Workspace bytes spava_score_topk needs for the query rows' softmax
+ * normalisers over each block, rounded up to 256: float32 plans keep one
+ * log-sum-exp per row, float32 [V][Hkv][n_q*G]; bf16 plans keep a (max, sum)
+ * pair per row and key chunk of the block, float32 [C][V][Hkv][n_q*G][2]
+ * with C = ceil(L/512) for L <= 8192 (chunks of 512 keys), else
+ * C = ceil(T / ceil(T/16)) with T = ceil(L/64) (at most 16 chunks).
  */
 size_t spava_score_topk_ws_bytes(const spava_plan* plan);
 

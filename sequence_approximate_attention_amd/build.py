@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspava.so")
-SOURCES = ["api.hip", "attn_bf16.hip", "rowstat_bf16.hip", "attn_f32.hip", "score.hip", "aux.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "score_bf16.hip", "attn_f32.hip", "score.hip", "aux.hip"]
 ARCH = os.environ.get("SPAVA_ARCH", "gfx950")
 
 # Packed-FP32 instructions are disabled for the device code: plain float math

@@ -47,9 +47,9 @@ int check_plan(const spava_plan* p) {
   return SPAVA_OK;
 }
 
-// rows_per_unit: query rows per workgroup of the kernel the arguments are
-// for (0 = the attention kernel of the plan's dtype).
-AttnArgs make_args(const spava_plan* p, int rows_per_unit = 0) {
+// Launch arguments of a plan; units are sized for the attention kernel of the
+// plan's dtype.
+AttnArgs make_args(const spava_plan* p) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.Hq = p->n_q_heads;
@@ -66,8 +66,7 @@ AttnArgs make_args(const spava_plan* p, int rows_per_unit = 0) {
   a.scale_log2 = a.scale * 1.44269504088896340736f;
   a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
   a.f32 = p->dtype == SPAVA_F32;
-  const int bm = rows_per_unit > 0 ? rows_per_unit
-                                   : (a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit());
+  const int bm = a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit();
   a.rows_per_unit = bm;
   a.n_ctx_units_per_host = ceil_div(a.L, bm) * a.Hq;
   a.n_q_units = ceil_div(a.nq * a.G, bm) * a.Hkv;
@@ -75,9 +74,15 @@ AttnArgs make_args(const spava_plan* p, int rows_per_unit = 0) {
   return a;
 }
 
+// Scoring workspace: float32 inputs keep one log2-domain LSE per (block, KV
+// head, query row); bf16 inputs keep a (max, sum) pair per key chunk.
 size_t stats_bytes(const spava_plan* p) {
   const size_t R = (size_t)p->n_query * (p->n_q_heads / p->n_kv_heads);
-  return ((size_t)p->n_hosts * p->n_kv_heads * R * sizeof(float) + 255) / 256 * 256;
+  const size_t rows = (size_t)p->n_hosts * p->n_kv_heads * R;
+  const size_t bytes = p->dtype == SPAVA_F32
+                           ? rows * sizeof(float)
+                           : rows * (size_t)score_bf16_key_chunks(p->host_len) * sizeof(float2);
+  return (bytes + 255) / 256 * 256;
 }
 
 size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
@@ -128,21 +133,21 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float
   if (ws_bytes < stats_bytes(plan))
     return fail(SPAVA_EWORKSPACE, "spava_score_topk: workspace %zu < %zu bytes", ws_bytes, stats_bytes(plan));
   hipStream_t s = (hipStream_t)stream;
-  AttnArgs a = make_args(plan, plan->dtype == SPAVA_F32 ? 0 : rowstat_bf16_rows_per_unit());
+  AttnArgs a = make_args(plan);
   a.q = q;
   a.k = k;
-  a.stats = (float*)ws;
   hipError_t e = hipSuccess;
-  if (a.nq > 0) {
-    if (a.f32) {
+  if (a.f32) {
+    a.stats = (float*)ws;
+    if (a.nq > 0) {
       e = launch_rowstat_f32(a, s);
-    } else {
-      e = launch_rowstat_bf16(a, s);
+      if (e != hipSuccess) return launched(e, "row statistics");
     }
-    if (e != hipSuccess) return launched(e, "row statistics");
+    e = launch_colsum_f32(a, scores, s);
+  } else {
+    e = launch_score_bf16(a, (float2*)ws, scores, s);
   }
-  e = launch_colsum(a, scores, s);
-  if (e != hipSuccess) return launched(e, "column sums");
+  if (e != hipSuccess) return launched(e, "block scores");
   e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);
   return launched(e, "top-lp selection");
 }

@@ -35,7 +35,7 @@
 // maxima.  When a tile breaks the bound, its row maxima become the reference,
 // the row sums are rescaled, the tile's probabilities are recomputed, and the
 // output wave rescales O just before adding them.
-#include "spava_common.h"
+#include "lds_dma.h"
 
 namespace spava {
 namespace {
@@ -62,10 +62,6 @@ struct Geo {
   static constexpr int VINST = VBYTES / 1024 / kPairs;
 };
 
-__device__ __forceinline__ int perm_row(int m) {  // swap bits 2 and 3
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
 __device__ __forceinline__ int wave_reduce_min(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
@@ -75,22 +71,6 @@ __device__ __forceinline__ int wave_reduce_max(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
   return x;
-}
-
-// 16-byte slot of chunk c in a swizzled LDS row r of RB bytes.
-template <int RB>
-__device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (RB == 256) return c ^ (r & 15);
-  else return c ^ ((r >> 1) & 7);
-}
-
-
-// s_waitcnt immediate (gfx9 encoding) that waits until at most N
-// vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // The unit's key runs as scalar fields (selected by value, never by a
@@ -228,37 +208,6 @@ __device__ __forceinline__ TileRef tile_ref(const Runs& R, int i) {
   r.run.tok0 = uni(r.run.tok0);
   r.kb0 = uni(live ? t * kBN : 0);
   return r;
-}
-
-// Raw buffer descriptor (gfx9 family: stride 0, word 3 = 0x00020000) over
-// `bytes` bytes from `base`, as four scalar words; loads at offsets past the
-// range return zero without touching memory.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  u32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((unsigned)b);
-  r.y = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu);
-  r.z = __builtin_amdgcn_readfirstlane(bytes);
-  r.w = 0x00020000u;
-  return r;
-}
-
-// One buffer_load_dwordx4 ... lds: every lane's 16 bytes at byte offset
-// soff + voff of the buffer land at lds + 16 * lane.  Written as inline
-// assembly so that the compiler keeps no wait bookkeeping of its own for these
-// copies: their completion is awaited explicitly (wait_vm) before the barrier
-// that publishes a ring slot.  M0 carries the LDS address; it needs one wait
-// state before the load.
-__device__ __forceinline__ void copy16_to_lds(const u32x4& rsrc, unsigned soff, unsigned voff,
-                                              unsigned lds) {
-  asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-      : "memory", "m0");
 }
 
 // Per-lane parts of the copy addresses.  A copy instruction moves 1 KB: R

@@ -5,10 +5,11 @@
 // query-to-context attention scores).  For block h and KV head g the score of
 // key j is the sum over the query block's rows r = (token i, head a in g) of
 // softmax_j(q_r . k_j * scale) over the block's L keys.  It takes two passes
-// over the block: the row log-sum-exp (the attention kernel's statistics
-// mode, or rowstat_f32 below), then the column sums here.  Probabilities are
-// float32, column sums accumulate in float64 in a fixed order, so the result
-// is deterministic and its relative error stays far below 1e-6.
+// over the block: the row log-sum-exp, then the column sums.  This file holds
+// the float32 path (vector ALUs) and the top-lp selection; bf16 inputs use the
+// MFMA kernels of score_bf16.hip.  Probabilities are float32, column sums
+// accumulate in float64 in a fixed order, so the result is deterministic and
+// its relative error stays far below 1e-6.
 //
 // Selection (ArgTop_lp in the APB-V review's axiom ledger): an exact radix
 // select on the order-preserving integer image of the float32 scores finds
@@ -18,89 +19,6 @@
 
 namespace spava {
 namespace {
-
-constexpr int kColThreads = 256;
-constexpr int kColKeys = 256;  // keys per workgroup (64 per wave)
-
-// S = Q K^T with the packed query rows as the A operand and the workgroup's
-// keys as the B operand (each wave holds 64 keys' fragments in registers);
-// Q tiles of 32 rows and their log2-domain LSE are staged in LDS.
-template <int D>
-__global__ __launch_bounds__(kColThreads) void colsum_bf16_kernel(AttnArgs a, float* __restrict__ scores) {
-  constexpr int NC = D / 16;
-  constexpr int QS = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * QS];
-  __shared__ float sL[32];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hi = lane >> 5;
-  const int col = lane & 31;
-  const int hg = blockIdx.y;  // h * Hkv + g
-  const int h = hg / a.Hkv;
-  const int g = hg % a.Hkv;
-  const int R = a.nq * a.G;
-  const long kstr = (long)a.Hkv * D;
-  const int key0 = blockIdx.x * kColKeys + wave * 64;
-  const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
-
-  bf16x8 kf[2][NC];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int j = min(key0 + 32 * kb + col, a.L - 1);
-    const uint16_t* kr = kbase + (long)j * kstr + 8 * hi;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kf[kb][c] = *(const bf16x8*)(kr + 16 * c);
-  }
-  double acc[2] = {0.0, 0.0};
-  const float sl2 = a.scale_log2;
-  const float* lse2 = a.stats + (long)hg * R;
-  const int q0 = a.la + a.V * a.L;
-
-  for (int r0 = 0; r0 < R; r0 += 32) {
-    __syncthreads();
-    constexpr int CPR = D / 8;
-    for (int ch = tid; ch < 32 * CPR; ch += kColThreads) {
-      const int rr = ch / CPR;
-      const int c = ch % CPR;
-      const int r = r0 + rr;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (r < R) {
-        const int tok = q0 + r % a.nq;
-        const int head = g * a.G + r / a.nq;
-        x = *(const uint4*)((const uint16_t*)a.q + ((long)tok * a.Hq + head) * D + c * 8);
-      }
-      *(uint4*)(sQ + rr * QS + c * 8) = x;
-    }
-    if (tid < 32) sL[tid] = (r0 + tid < R) ? lse2[r0 + tid] : INFINITY;
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-      const uint16_t* qr = sQ + col * QS + 8 * hi;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 qa = *(const bf16x8*)(qr + 16 * c);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][c], s, 0, 0, 0);
-      }
-      float part = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = (i >> 2) * 8 + hi * 4 + (i & 3);   // query row of accumulator i
-        part += __builtin_amdgcn_exp2f(s[i] * sl2 - sL[m]);
-      }
-      acc[kb] += (double)part;
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const double tot = acc[kb] + __shfl_xor(acc[kb], 32);
-    const int j = key0 + 32 * kb + col;
-    if (hi == 0 && j < a.L) scores[(long)hg * a.L + j] = (float)tot;
-  }
-}
 
 // float32 inputs: row statistics and column sums on the vector ALUs.
 template <int D>
@@ -308,26 +226,18 @@ hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s) {
 
 // Column sums; a.stats must already hold the row statistics.  With an empty
 // query block every score is 0 (a sum over no rows).
-hipError_t launch_colsum(const AttnArgs& a, float* scores, hipStream_t s) {
+hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s) {
   const long n = (long)a.V * a.Hkv * a.L;
   if (n == 0) return hipSuccess;
   if (a.nq * a.G == 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, scores, n);
     return hipGetLastError();
   }
-  if (a.f32) {
-    const dim3 grid((unsigned)((n + 255) / 256));
-    if (a.D == 128)
-      hipLaunchKernelGGL((colsum_f32_kernel<128>), grid, dim3(256), 0, s, a, scores);
-    else
-      hipLaunchKernelGGL((colsum_f32_kernel<64>), grid, dim3(256), 0, s, a, scores);
-  } else {
-    dim3 grid(ceil_div(a.L, kColKeys), a.V * a.Hkv);
-    if (a.D == 128)
-      hipLaunchKernelGGL((colsum_bf16_kernel<128>), grid, dim3(kColThreads), 0, s, a, scores);
-    else
-      hipLaunchKernelGGL((colsum_bf16_kernel<64>), grid, dim3(kColThreads), 0, s, a, scores);
-  }
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (a.D == 128)
+    hipLaunchKernelGGL((colsum_f32_kernel<128>), grid, dim3(256), 0, s, a, scores);
+  else
+    hipLaunchKernelGGL((colsum_f32_kernel<64>), grid, dim3(256), 0, s, a, scores);
   return hipGetLastError();
 }
 

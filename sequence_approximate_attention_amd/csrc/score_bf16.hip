@@ -1,0 +1,421 @@
+// Block scoring for bf16 inputs on gfx950 (CDNA4).
+//
+// The selection rule (Figure 5 caption of the Spava page: the query rows'
+// Q K^(h)T estimate how important block h's keys are; "What carries the
+// argument" in the APB-V review: keys ranked by query-to-context attention
+// scores) needs, for block h and KV head g, the column sums over the query
+// rows r = (token i, head a in g) of softmax_j(q_r . k_j * scale) over the
+// block's L keys.  Two MFMA passes over the block:
+//
+//   rowstat_chunk_kernel: each query row's running (max, sum) of
+//     exp2(s * scale * log2 e) over one key chunk of the block (512 keys, or
+//     L/16 for longer blocks).  A workgroup
+//     is 4 waves x 64 rows; the chunk is walked in 64-key tiles that
+//     buffer_load_dwordx4 ... lds copies into a 4-slot LDS ring, three tiles
+//     ahead.  Splitting the block into chunks gives the GPU enough
+//     workgroups; the partial (max, sum) pairs are combined by the next pass.
+//
+//   colsum_kernel: combines each row's chunk partials into its log2-domain
+//     log-sum-exp, then for 256 keys per workgroup sums exp2(s - lse) over all
+//     rows.  Each wave keeps 64 keys' fragments in registers; the two halves
+//     of the workgroup (4 waves each) take alternate 32-row chunks, whose Q
+//     tiles are copied into a 3-slot LDS ring per half, two chunks ahead.
+//     Column sums accumulate per chunk in float32, across chunks in float64,
+//     in a fixed order (deterministic).
+#include "lds_dma.h"
+
+namespace spava {
+namespace {
+
+constexpr int kBN = kKeyTile;
+constexpr float kGrowLog2 = 8.0f;
+
+// ---------------------------------------------------------------------------
+// Row statistics over key chunks.
+
+constexpr int kRsWaves = 4;
+constexpr int kRsWaveRows = 64;                  // two 32-column MFMA blocks
+constexpr int kRsBM = kRsWaves * kRsWaveRows;    // rows per workgroup
+constexpr int kRsThreads = kRsWaves * 64;
+constexpr int kRsSlots = 4;                      // K tile ring
+constexpr int kTilesPerChunk = 8;                // 512 keys per chunk (at least)
+
+template <int D>
+struct RsGeo {
+  static constexpr int NC = D / 16;              // 16-wide d chunks
+  static constexpr int KRB = 2 * D;              // bytes per K row
+  static constexpr int KBYTES = kBN * KRB;       // K tile
+  static constexpr int RPI = 1024 / KRB;         // K rows per copy instruction
+  static constexpr int KINST = KBYTES / 1024 / kRsWaves;
+};
+
+// Query row r of group g: token q0 + r % nq, head g * G + r / nq.
+__device__ __forceinline__ long q_row_elem(const AttnArgs& a, int g, int r) {
+  const int tok = a.la + a.V * a.L + r % a.nq;
+  const int head = g * a.G + r / a.nq;
+  return ((long)tok * a.Hq + head) * a.D;
+}
+
+// This wave's share of the copy of tile t of the chunk into kbuf; past the
+// chunk's last tile (t >= nt) the copy reads an empty range (zeros), so every
+// iteration issues the same number of copies.
+template <int D>
+__device__ __forceinline__ void rs_issue(const u32x4& rs_blk, int kstride2, int t0, int t, int nt,
+                                         char* kbuf, int wave, int lane) {
+  using G = RsGeo<D>;
+  u32x4 rs = rs_blk;
+  if (t >= nt) rs.z = 0;
+  const int q = lane / (G::KRB / 16);            // row within the copy
+  const int slot = lane % (G::KRB / 16);
+#pragma unroll
+  for (int j = 0; j < G::KINST; ++j) {
+    const int blk = wave * G::KINST + j;
+    const int row = blk * G::RPI + q;            // tile row
+    const int chunk = swz<G::KRB>(row, slot);    // source 16-byte chunk stored at this slot
+    copy16_to_lds(rs, (unsigned)((t0 + t) * kBN * kstride2), (unsigned)(row * kstride2 + chunk * 16),
+                  (unsigned)(unsigned long long)(kbuf + blk * 1024));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a, int KC, int TPC, int RT,
+                                                                       float2* __restrict__ part) {
+  using G = RsGeo<D>;
+  constexpr int NC = G::NC;
+  constexpr int KRB = G::KRB;
+  __shared__ __attribute__((aligned(1024))) char sK[kRsSlots * G::KBYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  const int R = a.nq * a.G;
+  const int VH = a.V * a.Hkv;
+
+  // Unit b = ((h * Hkv + g) * KC + kc) * RT + rt: the row tiles of one key
+  // chunk are consecutive (and dealt to one XCD).
+  const int n_units = VH * KC * RT;
+  const int b = xcd_unit(blockIdx.x, RT);
+  if (b >= n_units) return;
+  const int rt = b % RT;
+  const int kc = (b / RT) % KC;
+  const int hg = b / (RT * KC);
+  const int h = hg / a.Hkv;
+  const int g = hg % a.Hkv;
+
+  // This lane's two query rows (one per 32-column block).
+  int r[2];
+  bf16x8 qf[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    r[qb] = rt * kRsBM + wave * kRsWaveRows + 32 * qb + col;
+    const bool valid = r[qb] < R;
+    const uint16_t* qp = (const uint16_t*)a.q + q_row_elem(a, g, valid ? r[qb] : 0) + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[qb][c] = *(const bf16x8*)(qp + 16 * c);
+      if (!valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qb][c][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  // The chunk's tiles [t0, t0 + nt) of block h; keys past the block's end
+  // read as zero and are masked.
+  const int T = ceil_div(a.L, kBN);
+  const int t0 = kc * TPC;
+  const int nt = min(T, t0 + TPC) - t0;
+  const int kstride2 = a.Hkv * D * 2;
+  const uint16_t* kblk = (const uint16_t*)a.k + ((long)(a.la + h * a.L) * a.Hkv + g) * D;
+  const u32x4 rs_blk = make_rsrc(kblk, (unsigned)a.L * (unsigned)kstride2);
+
+  // The compiler's own wait bookkeeping does not see the LDS copies: settle
+  // the Q loads here so that no full wait lands inside the tile loop.
+  wait_vm<0>();
+
+  const int krow = perm_row(col);
+  int koff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = krow * KRB + swz<KRB>(krow, 2 * c + hi) * 16;
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  const float sl2 = a.scale_log2;
+#pragma unroll
+  for (int t = 0; t < kRsSlots - 1; ++t) rs_issue<D>(rs_blk, kstride2, t0, t, nt, sK + t * G::KBYTES, wave, lane);
+
+  for (int t = 0; t < nt; ++t) {
+    wait_vm<(kRsSlots - 2) * G::KINST>();   // tile t has landed (this wave's part)
+    __syncthreads();                          // ... everyone's; slot of t-1 is free
+    const int tn = t + kRsSlots - 1;
+    rs_issue<D>(rs_blk, kstride2, t0, tn, nt, sK + (tn % kRsSlots) * G::KBYTES, wave, lane);
+    const char* kt = sK + (t % kRsSlots) * G::KBYTES;
+
+    f32x16 s[2][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 af = *(const bf16x8*)(kt + koff[c] + h2 * 32 * KRB);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][c], c == 0 ? f32x16{} : s[qb][h2], 0, 0, 0);
+      }
+    const int lim = a.L - (t0 + t) * kBN;   // tile-local key j is in the block iff j < lim
+    if (lim < kBN) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = 32 * h2 + (e & 7) + 8 * hi + 16 * (e >> 3);
+            if (j >= lim) s[qb][h2][e] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][h2][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      if (__any(mx > m[qb] + kGrowLog2)) {
+        const float m_new = fmaxf(m[qb], mx);
+        l[qb] *= (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qb] - m_new);
+        m[qb] = m_new;
+      }
+      const float m_use = (m[qb] == -INFINITY) ? 0.0f : m[qb];
+      float psum = 0.0f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) psum += __builtin_amdgcn_exp2f(fmaf(s[qb][h2][e], sl2, -m_use));
+      l[qb] += psum;
+    }
+  }
+  wait_vm<0>();   // no copy may still be landing in LDS when the workgroup ends
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    if (hi == 0 && r[qb] < R) part[((long)kc * VH + hg) * R + r[qb]] = make_float2(m[qb], lt);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column sums.
+
+constexpr int kCsHalves = 2;
+constexpr int kCsWavesPerHalf = 4;
+constexpr int kCsThreads = kCsHalves * kCsWavesPerHalf * 64;
+constexpr int kCsKeys = kCsWavesPerHalf * 64;    // keys per workgroup
+constexpr int kCsRows = 32;                      // rows per chunk
+constexpr int kCsSlots = 3;                      // Q tile ring per half
+constexpr int kCsLseRows = 4096;                 // rows of the LSE table per pass
+constexpr int kMaxKeyChunks = 16;                // key chunks per block (L <= 8192)
+
+template <int D>
+struct CsGeo {
+  static constexpr int NC = D / 16;
+  static constexpr int QRB = 2 * D;                          // bytes per Q row
+  static constexpr int QBYTES = kCsRows * QRB;               // Q tile of one chunk
+  static constexpr int RPI = 1024 / QRB;                     // rows per copy instruction
+  static constexpr int QINST = QBYTES / 1024 / kCsWavesPerHalf;
+};
+
+// This wave's share of the copy of the Q rows [r0, r0 + 32) into qbuf
+// (rows at or past R read as zero).  Row r is token r % nq of head
+// g * G + r / nq; one division per chunk, then each lane steps from r0.
+template <int D>
+__device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, int g, int r0, int R,
+                                         char* qbuf, int w4, int lane) {
+  using G = CsGeo<D>;
+  const int q = lane / (G::QRB / 16);
+  const int slot = lane % (G::QRB / 16);
+  const int i0 = r0 % a.nq;
+  const int a0 = r0 / a.nq;
+#pragma unroll
+  for (int j = 0; j < G::QINST; ++j) {
+    const int blk = w4 * G::QINST + j;
+    const int row = blk * G::RPI + q;   // row within the chunk
+    int tok = i0 + row, head = a0;
+    while (tok >= a.nq) {               // at most 32 / nq + 1 steps
+      tok -= a.nq;
+      ++head;
+    }
+    const int chunk = swz<G::QRB>(row, slot);
+    const unsigned voff = (r0 + row < R)
+                              ? (unsigned)(((tok * a.Hq + g * a.G + head) * D) * 2 + chunk * 16)
+                              : rs_q.z;   // past the range: zeros
+    copy16_to_lds(rs_q, 0u, voff, (unsigned)(unsigned long long)(qbuf + blk * 1024));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int KC,
+                                                               const float2* __restrict__ part,
+                                                               float* __restrict__ scores) {
+  using G = CsGeo<D>;
+  constexpr int NC = G::NC;
+  constexpr int QRB = G::QRB;
+  __shared__ __attribute__((aligned(1024))) char sQ[kCsHalves * kCsSlots * G::QBYTES];
+  __shared__ __attribute__((aligned(16))) float sLse[kCsLseRows];
+  __shared__ double sAcc[kCsWavesPerHalf * 2 * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave / kCsWavesPerHalf;
+  const int w4 = wave % kCsWavesPerHalf;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  const int hg = blockIdx.y;   // h * Hkv + g
+  const int h = hg / a.Hkv;
+  const int g = hg % a.Hkv;
+  const int R = a.nq * a.G;
+  const int VH = a.V * a.Hkv;
+  const long kstr = (long)a.Hkv * D;
+  const int key0 = blockIdx.x * kCsKeys + w4 * 64;
+  const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
+
+  // This wave's 64 keys as B-operand fragments (K^T: 16 channels x 32 keys).
+  bf16x8 kf[2][NC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = min(key0 + 32 * kb + col, a.L - 1);
+    const uint16_t* kr = kbase + (long)j * kstr + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kf[kb][c] = *(const bf16x8*)(kr + 16 * c);
+  }
+  wait_vm<0>();   // as in the row statistics: no compiler wait inside the chunk loop
+
+  const u32x4 rs_q = make_rsrc((const uint16_t*)a.q + (long)(a.la + a.V * a.L) * a.Hq * D,
+                               (unsigned)a.nq * (unsigned)a.Hq * (unsigned)D * 2u);
+  char* const myq = sQ + half * kCsSlots * G::QBYTES;
+  const float sl2 = a.scale_log2;
+  double acc[2] = {0.0, 0.0};
+
+  for (int rb = 0; rb < R; rb += kCsLseRows) {
+    const int nrows = min(kCsLseRows, R - rb);
+    const int nch = ceil_div(nrows, kCsRows);
+    const int nj = ceil_div(nch, kCsHalves);   // chunks per half (the last may be empty)
+    __syncthreads();                           // previous pass done with sLse
+    // Q tiles of this half's first chunks (chunk c = 2j + half) ...
+#pragma unroll
+    for (int j = 0; j < kCsSlots - 1; ++j) {
+      const int c = kCsHalves * j + half;
+      cs_issue<D>(a, rs_q, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
+    }
+    // ... while the row LSEs are combined from the chunk partials:
+    // lse = M + log2(sum_k l_k 2^(m_k - M)); rows past R get +inf (weight 0).
+    // All of a row's partials are loaded at once (KC <= kMaxKeyChunks).
+    for (int i = tid; i < nch * kCsRows; i += kCsThreads) {
+      const int rr = rb + i;
+      float lse = INFINITY;
+      if (rr < R) {
+        float2 pk[kMaxKeyChunks];
+#pragma unroll
+        for (int k = 0; k < kMaxKeyChunks; ++k)
+          pk[k] = (k < KC) ? part[((long)k * VH + hg) * R + rr] : make_float2(-INFINITY, 0.0f);
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMaxKeyChunks; ++k) M = fmaxf(M, pk[k].x);
+        float lt = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kMaxKeyChunks; ++k)
+          if (pk[k].y > 0.0f) lt += pk[k].y * __builtin_amdgcn_exp2f(pk[k].x - M);
+        if (lt > 0.0f) lse = M + __log2f(lt);
+      }
+      sLse[i] = lse;
+    }
+    for (int j = 0; j < nj; ++j) {
+      wait_vm<G::QINST>();   // chunk j of this half has landed (this wave's part)
+      __syncthreads();       // ... everyone's, and the LSE table; slot of j-1 is free
+      {
+        const int jn = j + kCsSlots - 1;
+        const int cn = kCsHalves * jn + half;
+        cs_issue<D>(a, rs_q, g, (jn < nj && cn < nch) ? rb + cn * kCsRows : R, R,
+                    myq + (jn % kCsSlots) * G::QBYTES, w4, lane);
+      }
+      const int c = kCsHalves * j + half;
+      if (c >= nch) continue;
+      const char* qt = myq + (j % kCsSlots) * G::QBYTES;
+      // LSE of this lane's accumulator rows m = 8 * (i / 4) + 4 * hi + i % 4.
+      f32x4 lz[4];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) lz[gi] = *(const f32x4*)(sLse + c * kCsRows + 8 * gi + 4 * hi);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s;
+#pragma unroll
+        for (int c16 = 0; c16 < NC; ++c16) {
+          const bf16x8 qa = *(const bf16x8*)(qt + col * QRB + swz<QRB>(col, 2 * c16 + hi) * 16);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][c16], c16 == 0 ? f32x16{} : s, 0, 0, 0);
+        }
+        float pz = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pz += __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lz[i >> 2][i & 3]));
+        acc[kb] += (double)pz;
+      }
+    }
+    wait_vm<0>();
+  }
+
+  // Column totals: the lane pair (l, l^32) holds the two row halves of a
+  // key's accumulator rows; the second workgroup half's totals are added to
+  // the first's in a fixed order.
+  double tot[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) tot[kb] = acc[kb] + __shfl_xor(acc[kb], 32);
+  __syncthreads();
+  if (half == 1) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sAcc[(w4 * 2 + kb) * 64 + lane] = tot[kb];
+  }
+  __syncthreads();
+  if (half == 0 && hi == 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int j = key0 + 32 * kb + col;
+      if (j < a.L) scores[(long)hg * a.L + j] = (float)(tot[kb] + sAcc[(w4 * 2 + kb) * 64 + lane]);
+    }
+  }
+}
+
+}  // namespace
+
+// Key chunks per block: 512 keys each, but at most kMaxKeyChunks (longer
+// blocks get proportionally longer chunks).
+int score_bf16_tiles_per_chunk(int L) {
+  const int T = ceil_div(L, kBN);
+  return max(kTilesPerChunk, ceil_div(T, kMaxKeyChunks));
+}
+int score_bf16_key_chunks(int L) { return ceil_div(ceil_div(L, kBN), score_bf16_tiles_per_chunk(L)); }
+
+hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
+  const int R = a.nq * a.G;
+  const int VH = a.V * a.Hkv;
+  const int KC = score_bf16_key_chunks(a.L);
+  const int TPC = score_bf16_tiles_per_chunk(a.L);
+  if (R > 0) {
+    const int RT = ceil_div(R, kRsBM);
+    const int n = VH * KC * RT;
+    const dim3 grid(xcd_grid(n, RT));
+    if (a.D == 128)
+      hipLaunchKernelGGL((rowstat_chunk_kernel<128>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
+    else
+      hipLaunchKernelGGL((rowstat_chunk_kernel<64>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(ceil_div(a.L, kCsKeys), VH);
+  if (a.D == 128)
+    hipLaunchKernelGGL((colsum_kernel<128>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+  else
+    hipLaunchKernelGGL((colsum_kernel<64>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+  return hipGetLastError();
+}
+
+}  // namespace spava

@@ -5,8 +5,7 @@
 //     of key segments those rows attend to;
 //   * the kinds of unit follow the method's row types: anchor tokens,
 //     context tokens of host h, and the query block's partials (partial 0 =
-//     anchor + query block, partial h+1 = block h), plus a statistics-only
-//     pass over block h used by scoring.
+//     anchor + query block, partial h+1 = block h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,7 +27,6 @@ enum UnitKind : int {
   kContext = 1,   // context tokens of host h
   kQueryHead = 2, // query partial 0: anchor + query block (causal)
   kQueryBlock = 3,// query partial h+1: block h in full
-  kStats = 4,     // row log-sum-exp of the query rows over block h (no output O)
 };
 
 inline __host__ __device__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -70,7 +68,7 @@ struct AttnArgs {
   float* lse;
   float* o_part;
   float* lse_part;
-  float* stats;        // kStats output: [V][Hkv][nq*G] log2-domain row LSE
+  float* stats;        // float32 scoring: [V][Hkv][nq*G] log2-domain row LSE
   int N, Hq, Hkv, G, D, la, V, L, nq, lp;
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
@@ -80,14 +78,13 @@ struct AttnArgs {
   int n_q_units;             // ceil(nq*G/BM) * Hkv, per query partial
   int n_anchor_units;        // ceil(la/BM) * Hq
   int rows_per_unit;         // BM
-  int stats_only;            // 1: launch covers kStats units only
   int f32;                   // 1: float32 elements, 0: bf16
   int xcd_chunk;             // units per XCD chunk (see xcd_unit)
 };
 
 struct Unit {
   int kind;
-  int host;      // kContext / kQueryBlock / kStats
+  int host;      // kContext / kQueryBlock
   int head;      // query head (single-head units)
   int group;     // KV head
   int tile;      // row tile index inside the unit's row space
@@ -97,7 +94,6 @@ struct Unit {
 //   context units of host V-1 down to 0 (later row tiles first, heads fastest),
 //   query-block partials of blocks 0..V-1, query partial 0, anchor units.
 // Query-row units are KV-group-major so that units sharing K/V are adjacent.
-// A stats launch covers V * n_q_units units, block-major.
 __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   Unit u;
   u.host = 0;
@@ -106,14 +102,6 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   u.tile = 0;
   const int bm = a.rows_per_unit;
   const int qt = a.n_q_units / a.Hkv;  // query row tiles per KV group
-  if (a.stats_only) {
-    u.kind = kStats;
-    u.host = b / a.n_q_units;
-    int r = b % a.n_q_units;
-    u.group = r / qt;
-    u.tile = r % qt;
-    return u;
-  }
   const int nctx = a.V * a.n_ctx_units_per_host;
   if (b < nctx) {
     u.kind = kContext;
@@ -152,7 +140,6 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
 }
 
 __host__ __device__ inline int attn_total_units(const AttnArgs& a) {
-  if (a.stats_only) return a.V * a.n_q_units;
   return a.V * a.n_ctx_units_per_host + a.V * a.n_q_units + a.n_q_units + a.n_anchor_units;
 }
 
@@ -234,7 +221,6 @@ __device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
       break;
     }
     case kQueryBlock:
-    case kStats:
       main_seg(a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
       break;
   }
@@ -268,12 +254,14 @@ __device__ inline RowId unit_row(const AttnArgs& a, const Unit& u, int r) {
 // ---- launchers (host), defined in the .hip files ----
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
-hipError_t launch_rowstat_bf16(const AttnArgs& a, hipStream_t s);   // kStats units
-int rowstat_bf16_rows_per_unit();
+// bf16 scoring (row statistics over key chunks, then column sums); part holds
+// score_bf16_key_chunks(L) * V * Hkv * nq * G (max, sum) pairs.
+hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s);
+int score_bf16_key_chunks(int L);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s);
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
-hipError_t launch_colsum(const AttnArgs& a, float* scores, hipStream_t s);
+hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);
 hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
                          int la, int V, int L, int Hkv, int lp, int row_bytes, hipStream_t s);

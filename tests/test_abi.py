@@ -62,8 +62,12 @@ def test_plan_check(kw, code):
 
 def test_workspace_sizes():
     p = plan(dtype=S.SPAVA_BF16, head_dim=128)
-    # row statistics: V * Hkv * n_q * G floats
-    assert S.spava_score_topk_ws_bytes(p) == 4 * 1 * 16 * 2 * 4
+    # bf16 scoring: a (max, sum) float pair per (key chunk of 512, block, KV head, query row)
+    assert S.spava_score_topk_ws_bytes(p) == 1 * 4 * 1 * 16 * 2 * 8
+    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16)) == 2 * 4 * 1 * 16 * 2 * 8
+    # float32 scoring: one log-sum-exp float per (block, KV head, query row), 256-byte rounded
+    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 16 * 2 * 4
+    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=3)) == 256
     # key-contiguous V: Hkv * d * (pad(la) + V*pad(L) + pad(n_q)) + passing, bf16
     main = 1 * 128 * (64 + 4 * 128 + 64) * 2
     pas = 1 * 128 * 64 * 2
