@@ -53,10 +53,11 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_qwen3b_32k_traffic.md
 ATTN_SOURCE = os.path.join(ROOT, "sequence_approximate_attention_amd", "csrc", "attn_bf16.hip")
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM-side bytes per attention launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was
-    taken on a different kernel source than the one built here."""
+    taken on another workload or a different kernel source than the one built
+    here."""
     import hashlib
     try:
         fields = {}
@@ -65,7 +66,7 @@ def measured_traffic():
                 key, val = line.strip().split(" = ", 1)
                 fields[key] = val
         src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if fields.get("kernel_source_sha256") != src:
+        if fields.get("kernel_source_sha256") != src or fields.get("workload") != workload:
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -129,7 +130,7 @@ def main():
     import sequence_approximate_attention_amd as S
     import workloads as W
 
-    wl = {w.name: w for w in W.WORKLOADS}[args.workload]
+    wl = {w.name: w for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS}[args.workload]
     x = W.make_inputs(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -207,7 +208,7 @@ def main():
                    "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(wl.name)},
         "attn_tflop_per_launch": F_attn / 1e12,
         "step_tflops": (F_attn + score_flops(wl)) / (ms_per_step * 1e-3) / 1e12,
         "stage_ms": stage_ms,

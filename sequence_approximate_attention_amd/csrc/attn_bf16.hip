@@ -21,8 +21,9 @@
 //   V^T tile [D][64 keys]   key-contiguous, read as the MFMA A operand of O^T
 //   P tile   [2][4][64 lanes][8 bf16]  already in the B-operand layout
 // K and V^T rows are XOR-swizzled in 16-byte slots (the 16 rows of one
-// ds_read_b128 phase land in distinct banks).  Tiles past the end of the walk
-// are copied from an empty range and fully masked.
+// ds_read_b128 phase land in distinct banks).  Every copy addresses memory
+// inside its tensor: tiles past the end of the walk re-read a tile already
+// visited, K rows past a run's end read its last row, and both are masked.
 //
 // Math: S^T = K Q^T puts one query column per lane, so a row's softmax
 // statistics live in one lane pair (l, l^32) of the softmax wave.  K-tile rows
@@ -237,13 +238,17 @@ __device__ __forceinline__ LaneCopy lane_copy(int lane) {
 
 // A cursor walking one operand's tiles through the unit's runs, in scalar
 // registers: moving to the next tile is an add and a subtract, and the run
-// table is only consulted when a run ends.
+// table is only consulted when a run ends.  Every copy addresses memory
+// inside its tensor: K rows past a run's end are read as the run's last row
+// (their logits are masked), and past the walk the cursor keeps pointing at a
+// tile it has already visited (or the unit's first run).
 struct Cursor {
   unsigned long long addr;  // K: first key row of the tile; V^T: its first key in channel row 0
   int rem;                  // bytes the copy may read from addr (0: nothing)
   int stride2;              // bytes between the rows a copy reads (K: keys; V^T: channels)
   int left;                 // tiles left in the current run, this one included
   int s;                    // current run; 3 = past the walk
+  int rows;                 // K: rows of the run from this tile on (0 past the walk)
 };
 
 // Enter run s (or the first later run that has tiles) at its first tile.
@@ -251,9 +256,10 @@ template <int D, bool IS_K>
 __device__ __forceinline__ void cursor_enter(Cursor& c, const Runs& R, int s) {
   while (s < 3 && pick3(R.r0.nt, R.r1.nt, R.r2.nt, s) == 0) ++s;
   c.s = s;
-  if (s >= 3) {
+  if (s >= 3) {          // past the walk: the cursor stays on its last tile
     c.rem = 0;
-    c.left = 1 << 30;
+    c.rows = 0;
+    c.left = 1;
     return;
   }
   const SegRun r = sel(R.r0, R.r1, R.r2, s);
@@ -261,12 +267,22 @@ __device__ __forceinline__ void cursor_enter(Cursor& c, const Runs& R, int s) {
   if (IS_K) {
     c.addr = (unsigned long long)uni(r.k);
     c.stride2 = uni(r.kstride) * 2;
-    c.rem = uni(r.len) * c.stride2;   // to the run's end: rows past it read as zero
+    c.rows = uni(r.len);
+    c.rem = c.rows * c.stride2;
   } else {
     c.addr = (unsigned long long)uni(r.vt);
     c.stride2 = uni(r.vrow) * 2;
     c.rem = (D - 1) * c.stride2 + kBN * 2;   // one zero-padded tile
   }
+}
+
+// Start a cursor at the unit's first run (the address stays valid even when
+// the walk is empty).
+template <int D, bool IS_K>
+__device__ __forceinline__ void cursor_start(Cursor& c, const Runs& R) {
+  c.addr = (unsigned long long)(IS_K ? uni(R.r0.k) : uni(R.r0.vt));
+  c.stride2 = IS_K ? uni(R.r0.kstride) * 2 : uni(R.r0.vrow) * 2;
+  cursor_enter<D, IS_K>(c, R, 0);
 }
 
 template <int D, bool IS_K>
@@ -276,6 +292,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const Runs& R) {
     if (IS_K) {
       c.addr += (unsigned long long)(kBN * c.stride2);
       c.rem -= kBN * c.stride2;
+      c.rows -= kBN;
     } else {
       c.addr += kBN * 2;
     }
@@ -294,15 +311,17 @@ __device__ __forceinline__ u32x4 cursor_rsrc(const Cursor& c) {
 }
 
 // Copy instruction j (of Geo::KINST) of this wave's share of the K tile at
-// the cursor; qoff = this lane's row within the copy * stride.
+// the cursor; the lane's tile row is clamped to the run's last row.
 template <int D>
-__device__ __forceinline__ void copy_k(const Cursor& c, int qoff, const LaneCopy& lc, int j,
-                                       const char* kbuf, int wave) {
+__device__ __forceinline__ void copy_k(const Cursor& c, const LaneCopy& lc, int j, const char* kbuf,
+                                       int wave) {
   using G = Geo<D>;
   constexpr int R = 1024 / G::KRB;            // rows per copy
   const int blk = wave * G::KINST + j;
   const int jx = (R == 4 ? j : (j & 1)) * 64;
-  copy16_to_lds(cursor_rsrc(c), (unsigned)(blk * R * c.stride2), (unsigned)(qoff + (lc.kx16 ^ jx)),
+  const int last = max(0, min(kBN, c.rows) - 1);
+  const int row = min(blk * R + lc.kq, last);
+  copy16_to_lds(cursor_rsrc(c), 0u, (unsigned)(row * c.stride2 + (lc.kx16 ^ jx)),
                 (unsigned)(unsigned long long)(kbuf + blk * 1024));
 }
 
@@ -320,9 +339,8 @@ __device__ __forceinline__ void copy_v(const Cursor& c, int qoff, const LaneCopy
 // The whole of this wave's share of one tile's copies at once (prologue).
 template <int D>
 __device__ __forceinline__ void issue_k(const Cursor& c, const LaneCopy& lc, char* kbuf, int wave) {
-  const int qoff = lc.kq * c.stride2;
 #pragma unroll
-  for (int j = 0; j < Geo<D>::KINST; ++j) copy_k<D>(c, qoff, lc, j, kbuf, wave);
+  for (int j = 0; j < Geo<D>::KINST; ++j) copy_k<D>(c, lc, j, kbuf, wave);
 }
 template <int D>
 __device__ __forceinline__ void issue_v(const Cursor& c, const LaneCopy& lc, char* vbuf, int wave) {
@@ -561,7 +579,7 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
       if (n >= 1 && n < 1 + G::VINST) copy_v<D>(vc, cx.lc.vq * vc.stride2, cx.lc, n - 1, vload, cx.w);
       if (n == G::VINST) cursor_next<D, false>(vc, run);
       if (n >= 1 + G::VINST && n < 1 + G::VINST + G::KINST)
-        copy_k<D>(kc, cx.lc.kq * kc.stride2, cx.lc, n - 1 - G::VINST, kload, cx.w);
+        copy_k<D>(kc, cx.lc, n - 1 - G::VINST, kload, cx.w);
       if (n == G::VINST + G::KINST) cursor_next<D, true>(kc, run);
     }
   } else {
@@ -755,8 +773,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
 
     // K(0) and K(1) ahead of iteration 0; the cursors then stand at K(2) and V(0).
     Cursor kc, vc;
-    cursor_enter<D, true>(kc, run, 0);
-    cursor_enter<D, false>(vc, run, 0);
+    cursor_start<D, true>(kc, run);
+    cursor_start<D, false>(vc, run);
     issue_k<D>(kc, cx.lc, sK, cx.w);
     cursor_next<D, true>(kc, run);
     issue_k<D>(kc, cx.lc, sK + G::KBYTES, cx.w);

@@ -31,8 +31,10 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Raw buffer descriptor (gfx9 family: stride 0, word 3 = 0x00020000) over
-// `bytes` bytes from `base`, as four scalar words; loads at offsets past the
-// range return zero without touching memory.
+// `bytes` bytes from `base`, as four scalar words.  The kernels keep every
+// lane's address of a direct-to-LDS copy inside its tensor and do not rely on
+// the range check: copies whose lanes pointed past the end of a tensor that
+// ended on an allocation boundary have faulted the GPU.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
   const unsigned long long b = (unsigned long long)base;

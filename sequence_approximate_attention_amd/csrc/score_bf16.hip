@@ -56,15 +56,16 @@ __device__ __forceinline__ long q_row_elem(const AttnArgs& a, int g, int r) {
   return ((long)tok * a.Hq + head) * a.D;
 }
 
-// This wave's share of the copy of tile t of the chunk into kbuf; past the
-// chunk's last tile (t >= nt) the copy reads an empty range (zeros), so every
+// This wave's share of the copy of tile t of the chunk into kbuf.  Every lane
+// addresses a key of the block: rows past the block's end read its last key
+// (their logits are masked), and past the chunk's last tile (t >= nt, a slot
+// that is never read) the copy re-reads the chunk's first tile, so every
 // iteration issues the same number of copies.
 template <int D>
-__device__ __forceinline__ void rs_issue(const u32x4& rs_blk, int kstride2, int t0, int t, int nt,
+__device__ __forceinline__ void rs_issue(const u32x4& rs_blk, int kstride2, int L, int t0, int t, int nt,
                                          char* kbuf, int wave, int lane) {
   using G = RsGeo<D>;
-  u32x4 rs = rs_blk;
-  if (t >= nt) rs.z = 0;
+  const int tt = t0 + (t < nt ? t : 0);          // tile of the block
   const int q = lane / (G::KRB / 16);            // row within the copy
   const int slot = lane % (G::KRB / 16);
 #pragma unroll
@@ -72,7 +73,8 @@ __device__ __forceinline__ void rs_issue(const u32x4& rs_blk, int kstride2, int 
     const int blk = wave * G::KINST + j;
     const int row = blk * G::RPI + q;            // tile row
     const int chunk = swz<G::KRB>(row, slot);    // source 16-byte chunk stored at this slot
-    copy16_to_lds(rs, (unsigned)((t0 + t) * kBN * kstride2), (unsigned)(row * kstride2 + chunk * 16),
+    const int key = min(tt * kBN + row, L - 1);
+    copy16_to_lds(rs_blk, 0u, (unsigned)(key * kstride2 + chunk * 16),
                   (unsigned)(unsigned long long)(kbuf + blk * 1024));
   }
 }
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   }
 
   // The chunk's tiles [t0, t0 + nt) of block h; keys past the block's end
-  // read as zero and are masked.
+  // are masked.
   const int T = ceil_div(a.L, kBN);
   const int t0 = kc * TPC;
   const int nt = min(T, t0 + TPC) - t0;
@@ -143,13 +145,13 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
   const float sl2 = a.scale_log2;
 #pragma unroll
-  for (int t = 0; t < kRsSlots - 1; ++t) rs_issue<D>(rs_blk, kstride2, t0, t, nt, sK + t * G::KBYTES, wave, lane);
+  for (int t = 0; t < kRsSlots - 1; ++t) rs_issue<D>(rs_blk, kstride2, a.L, t0, t, nt, sK + t * G::KBYTES, wave, lane);
 
   for (int t = 0; t < nt; ++t) {
     wait_vm<(kRsSlots - 2) * G::KINST>();   // tile t has landed (this wave's part)
     __syncthreads();                          // ... everyone's; slot of t-1 is free
     const int tn = t + kRsSlots - 1;
-    rs_issue<D>(rs_blk, kstride2, t0, tn, nt, sK + (tn % kRsSlots) * G::KBYTES, wave, lane);
+    rs_issue<D>(rs_blk, kstride2, a.L, t0, tn, nt, sK + (tn % kRsSlots) * G::KBYTES, wave, lane);
     const char* kt = sK + (t % kRsSlots) * G::KBYTES;
 
     f32x16 s[2][2];
@@ -225,9 +227,10 @@ struct CsGeo {
   static constexpr int QINST = QBYTES / 1024 / kCsWavesPerHalf;
 };
 
-// This wave's share of the copy of the Q rows [r0, r0 + 32) into qbuf
-// (rows at or past R read as zero).  Row r is token r % nq of head
-// g * G + r / nq; one division per chunk, then each lane steps from r0.
+// This wave's share of the copy of the Q rows [r0, r0 + 32) into qbuf.  Row r
+// is token r % nq of head g * G + r / nq (one division per chunk, then each
+// lane steps from r0); rows at or past R read row 0, a real row whose
+// probabilities the +inf LSE of those rows zeroes.
 template <int D>
 __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, int g, int r0, int R,
                                          char* qbuf, int w4, int lane) {
@@ -245,11 +248,13 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
       tok -= a.nq;
       ++head;
     }
+    if (r0 + row >= R) {
+      tok = 0;
+      head = 0;
+    }
     const int chunk = swz<G::QRB>(row, slot);
-    const unsigned voff = (r0 + row < R)
-                              ? (unsigned)(((tok * a.Hq + g * a.G + head) * D) * 2 + chunk * 16)
-                              : rs_q.z;   // past the range: zeros
-    copy16_to_lds(rs_q, 0u, voff, (unsigned)(unsigned long long)(qbuf + blk * 1024));
+    copy16_to_lds(rs_q, 0u, (unsigned)(((tok * a.Hq + g * a.G + head) * D) * 2 + chunk * 16),
+                  (unsigned)(unsigned long long)(qbuf + blk * 1024));
   }
 }
 

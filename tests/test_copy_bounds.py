@@ -1,0 +1,219 @@
+"""Every direct-to-LDS copy of the bf16 kernels addresses memory inside its
+tensor, on every workload shape, without relying on the buffer range check.
+
+The kernels' tile walks are re-derived here from their definitions (the unit
+order, each unit's key runs, the tile cursors of the attention kernel, the key
+chunks of the row statistics, the query-row chunks of the column sums) and
+every copy's byte range is checked against the tensor it reads.  Host logic
+only: no GPU is used.  A tensor whose size is a multiple of the allocator's
+2 MiB granule has no slack behind it, so a read past its end can fault; this
+is the check that would have caught such reads.
+"""
+import pytest
+
+import workloads as W
+
+KT = 64          # keys per tile
+BM = 256         # query rows per attention unit
+CS_ROWS = 32     # query rows per column-sum chunk
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def vt_layout(la, V, L, nq, lp):
+    pad = lambda n: cdiv(n, KT) * KT
+    off_block0 = pad(la)
+    off_query = pad(la) + V * pad(L)
+    return dict(pad_block=pad(L), off_block0=off_block0, off_query=off_query,
+                main_len=off_query + pad(nq), pass_len=pad(V * lp) or KT)
+
+
+class Extent:
+    def __init__(self, name, nbytes):
+        self.name, self.nbytes = name, nbytes
+
+    def check(self, lo, hi, what):
+        assert 0 <= lo and hi <= self.nbytes, f"{what}: {self.name} bytes [{lo}, {hi}) outside [0, {self.nbytes})"
+
+
+def attention_copies(w, D, past_walk="stay"):
+    """Walk the attention kernel's K and V^T cursors of every unit.  With
+    past_walk="advance" a cursor keeps stepping over whole tiles after the
+    walk (what a cursor whose remaining byte count had gone negative, read as
+    an unsigned range, would do); the kernels keep it on its last tile."""
+    la, V, L, nq, lp, Hq, Hkv = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.lp, w.n_q_heads, w.n_kv_heads
+    G = Hq // Hkv
+    N = la + V * L + nq
+    vl = vt_layout(la, V, L, nq, lp)
+    ext = {"k": Extent("k", N * Hkv * D * 2), "kp": Extent("kp", Hkv * V * lp * D * 2),
+           "vt": Extent("vt", Hkv * D * vl["main_len"] * 2), "vpt": Extent("vpt", Hkv * D * vl["pass_len"] * 2)}
+    n_ctx_h = cdiv(L, BM) * Hq
+    n_q = cdiv(nq * G, BM) * Hkv
+    qt = n_q // Hkv
+    n_units = V * n_ctx_h + V * n_q + n_q + cdiv(la, BM) * Hq
+    tiles = 0
+    for b in range(n_units):
+        if b < V * n_ctx_h:
+            kind, host = "ctx", V - 1 - b // n_ctx_h
+            r = b % n_ctx_h
+            head, tile = r % Hq, cdiv(L, BM) - 1 - r // Hq
+            g = head // G
+        elif b < V * n_ctx_h + V * n_q:
+            bb = b - V * n_ctx_h
+            kind, host, g, tile = "qblock", bb // n_q, (bb % n_q) // qt, (bb % n_q) % qt
+        elif b < V * n_ctx_h + V * n_q + n_q:
+            bb = b - V * n_ctx_h - V * n_q
+            kind, host, g, tile = "qhead", 0, bb // qt, bb % qt
+        else:
+            bb = b - V * n_ctx_h - V * n_q - n_q
+            kind, host = "anchor", 0
+            head, tile = bb % Hq, cdiv(la, BM) - 1 - bb // Hq
+            g = head // G
+        if kind in ("ctx", "anchor"):
+            base, n = (0, la) if kind == "anchor" else (la + host * L, L)
+            toks = [base + r for r in range(tile * BM, min(n, tile * BM + BM))]
+        else:
+            R = nq * G
+            toks = [la + V * L + r % nq for r in range(tile * BM, min(R, tile * BM + BM))]
+        if not toks:
+            continue
+        gmax = max(toks)
+
+        def main(tok0, n, vkey, causal):
+            return dict(kbuf="k", k=(tok0 * Hkv + g) * D * 2, vbuf="vt", vt=(g * D * vl["main_len"] + vkey) * 2,
+                        kstr=Hkv * D * 2, vstr=vl["main_len"] * 2, len=n, causal=causal, tok0=tok0)
+        runs = [main(0, 0, 0, 0)] * 3
+        if kind == "anchor":
+            runs = [main(0, la, 0, 1), dict(runs[1], len=0), dict(runs[2], len=0)]
+        elif kind == "ctx":
+            pas = dict(kbuf="kp", k=g * V * lp * D * 2, vbuf="vpt", vt=g * D * vl["pass_len"] * 2,
+                       kstr=D * 2, vstr=vl["pass_len"] * 2, len=host * lp if lp else 0, causal=0, tok0=0)
+            runs = [main(0, la, 0, 0), pas if host > 0 else dict(pas, len=0),
+                    main(la + host * L, L, vl["off_block0"] + host * vl["pad_block"], 1)]
+        elif kind == "qhead":
+            runs = [main(0, la, 0, 0), main(la + V * L, nq, vl["off_query"], 1), dict(runs[2], len=0)]
+        else:
+            runs = [main(la + host * L, L, vl["off_block0"] + host * vl["pad_block"], 0),
+                    dict(runs[1], len=0), dict(runs[2], len=0)]
+        nts = []
+        for x in runs:
+            n = min(x["len"], gmax - x["tok0"] + 1) if x["causal"] else x["len"]
+            nts.append(cdiv(n, KT) if n > 0 else 0)
+        T = sum(nts)
+
+        def walk(is_k):
+            """Byte ranges [lo, hi) and buffer of the copies issued for tiles 0 .. T+3."""
+            out = []
+            addr, stride, buf = ((runs[0]["k"], runs[0]["kstr"], "k") if is_k
+                                 else (runs[0]["vt"], runs[0]["vstr"], "vt"))
+            s, left, rows = 0, 0, 0
+
+            def enter(s0):
+                nonlocal s, left, rows, addr, stride, buf
+                s = s0
+                while s < 3 and nts[s] == 0:
+                    s += 1
+                if s >= 3:
+                    if past_walk == "stay":
+                        left, rows = 1, 0      # stays on its last tile
+                    else:
+                        left, rows = 1 << 30, 1 << 30
+                    return
+                x = runs[s]
+                left = nts[s]
+                if is_k:
+                    addr, stride, buf, rows = x["k"], x["kstr"], x["kbuf"], x["len"]
+                else:
+                    addr, stride, buf = x["vt"], x["vstr"], x["vbuf"]
+            enter(0)
+            for _ in range(T + 4):
+                if is_k:
+                    last = max(0, min(KT, rows) - 1)
+                    out.append((buf, addr, addr + last * stride + D * 2))
+                else:
+                    out.append((buf, addr, addr + (D - 1) * stride + KT * 2))
+                if left > 1:
+                    left -= 1
+                    if is_k:
+                        addr += KT * stride
+                        rows -= KT
+                    else:
+                        addr += KT * 2
+                else:
+                    enter(s + 1)
+            return out
+        for is_k in (True, False):
+            for buf, lo, hi in walk(is_k):
+                ext[buf].check(lo, hi, f"{w.name} unit {b} ({kind}) {'K' if is_k else 'V'} copy")
+                tiles += 1
+    return tiles
+
+
+def score_copies(w, D):
+    """Row statistics: K tiles of each key chunk; column sums: Q rows of each chunk."""
+    la, V, L, nq, Hq, Hkv = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.n_q_heads, w.n_kv_heads
+    G = Hq // Hkv
+    N = la + V * L + nq
+    R = nq * G
+    k = Extent("k", N * Hkv * D * 2)
+    q = Extent("q", N * Hq * D * 2)
+    if R == 0:
+        return 0
+    T = cdiv(L, KT)
+    tpc = max(8, cdiv(T, 16))
+    kc_n = cdiv(T, tpc)
+    kstr = Hkv * D * 2
+    n = 0
+    for h in range(V):
+        for g in range(Hkv):
+            kblk = ((la + h * L) * Hkv + g) * D * 2
+            for kc in range(kc_n):
+                t0 = kc * tpc
+                nt = min(T, t0 + tpc) - t0
+                for t in range(nt + 3):
+                    tt = t0 + (t if t < nt else 0)
+                    first, last = tt * KT, min(tt * KT + KT - 1, L - 1)
+                    k.check(kblk + first * kstr, kblk + last * kstr + D * 2, f"{w.name} row statistics h{h} g{g}")
+                    n += 1
+    q0 = (la + V * L) * Hq * D * 2
+    for g in range(Hkv):
+        for c in range(cdiv(R, CS_ROWS) + 2):
+            for row in range(CS_ROWS):
+                r = c * CS_ROWS + row
+                tok, head = (r % nq, g * G + r // nq) if r < R else (0, g * G)
+                off = q0 + (tok * Hq + head) * D * 2
+                q.check(off, off + D * 2, f"{w.name} column sums g{g} chunk {c}")
+            n += 1
+    return n
+
+
+SMALL = [
+    W.small_workload("bf16"),
+    W.small_workload("bf16", Hq=8, Hkv=2, d=64, la=0, V=4, L=77, n_q=9, lp=77, seed=8),
+    W.small_workload("bf16", Hq=7, Hkv=1, d=128, la=130, V=2, L=200, n_q=33, lp=0, seed=9),
+    W.small_workload("bf16", Hq=4, Hkv=4, d=128, la=5, V=5, L=64, n_q=1, lp=1, seed=10),
+    W.small_workload("bf16", Hq=2, Hkv=1, d=128, la=64, V=1, L=300, n_q=0, lp=17, seed=11),
+]
+FULL = [W.QWEN3B_32K, W.QWEN7B_64K, W.QWEN3B_128K, W.QWEN3B_128K.with_(lp=8064),
+        W.QWEN3B_32K_PAGE_DEFAULTS, W.QWEN3B_32K_PAGE_DEFAULTS_Q128, W.LLAMA8B_128K_TEXT]
+
+
+@pytest.mark.parametrize("w", SMALL + FULL, ids=lambda w: f"{w.name}_lp{w.lp}")
+def test_score_copies_in_bounds(w):
+    assert score_copies(w, w.head_dim) > 0 or w.n_query == 0
+
+
+@pytest.mark.parametrize("w", SMALL + FULL, ids=lambda w: f"{w.name}_lp{w.lp}")
+def test_attention_copies_in_bounds(w):
+    assert attention_copies(w, w.head_dim) > 0
+
+
+@pytest.mark.parametrize("w", [W.QWEN3B_32K_PAGE_DEFAULTS_Q128, W.LLAMA8B_128K_TEXT], ids=lambda w: w.name)
+def test_walk_catches_a_cursor_that_runs_past_the_walk(w):
+    # The query partials' last run ends at token N: stepping on past it reads
+    # beyond k.  Both of these shapes have k ending on a 2 MiB granule.
+    assert (w.n_tokens * w.n_kv_heads * w.head_dim * 2) % (2 << 20) == 0
+    with pytest.raises(AssertionError, match="outside"):
+        attention_copies(w, w.head_dim, past_walk="advance")

@@ -109,3 +109,18 @@ def test_qwen3b_128k_lp_sweep(lp):
 def test_qwen7b_256k_frames():
     w = W.QWEN7B_256K
     run_case(w, query_stride=17, stride=127, heads=[0, w.n_q_heads - 1])
+
+
+# The pages' default hyper-parameters (la = n/64, lp = n/128).
+def test_qwen3b_32k_page_defaults():
+    run_case(W.QWEN3B_32K_PAGE_DEFAULTS, query_stride=3)
+
+
+# Host blocks of 4016 keys (not whole tiles), 128-token query block.
+def test_qwen3b_32k_page_defaults_q128():
+    run_case(W.QWEN3B_32K_PAGE_DEFAULTS_Q128, query_stride=1)
+
+
+def test_llama8b_128k_text():
+    w = W.LLAMA8B_128K_TEXT
+    run_case(w, query_stride=5, stride=127, heads=[0, 13, w.n_q_heads - 1])

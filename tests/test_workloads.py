@@ -11,9 +11,19 @@ def test_shapes_and_token_counts():
     assert W.QWEN7B_64K.n_tokens == 65792
     assert W.QWEN3B_128K.n_tokens == 131200
     assert W.QWEN7B_256K.n_tokens == 264704
-    for w in W.WORKLOADS:
+    for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS:
         assert w.n_q_heads % w.n_kv_heads == 0
         assert 0 <= w.lp <= w.host_len
+
+
+def test_page_default_ratios():
+    # la = n/64 and lp = n/128 of the whole input length, 8 hosts.
+    for w in W.PAGE_DEFAULT_WORKLOADS:
+        n = w.n_tokens
+        assert n % 128 == 0
+        assert w.n_anchor * 64 == n and w.lp * 128 == n and w.n_hosts == 8
+    assert W.LLAMA8B_128K_TEXT.n_tokens == 131072
+    assert (W.LLAMA8B_128K_TEXT.n_q_heads, W.LLAMA8B_128K_TEXT.n_kv_heads) == (32, 8)
 
 
 def test_determinism_and_seed_dependence():

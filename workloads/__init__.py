@@ -73,6 +73,29 @@ QWEN7B_256K = Workload("qwen2.5vl7b_256k_frames", BF16, 28, 4, 128, 4096, 32, 81
 WORKLOADS = [TINY_F32, QWEN3B_32K, QWEN7B_64K, QWEN3B_128K, QWEN7B_256K]
 QWEN3B_128K_LP_SWEEP = (512, 2048, 8064)
 
+# The pages' default hyper-parameters (APB-V review, free-parameter ledger:
+# anchor length la = n/64, passing length lp = n/128, H = 8 hosts), with n the
+# whole input length, on two shapes:
+#  * the 32K video layer above, re-split at n = 32768 (la 512, lp 256);
+#  * a text-shaped layer standing in for the pages' long-context NLP transfer
+#    (RULER at 128K input, Llama-3.1-8B, 8 GPUs): 128K tokens, 32 query / 8 KV
+#    heads of width 128 (the public Llama-3.1-8B configuration; the pages give
+#    no head counts) and a 64-key needle in place of the benchmark's
+#    needle-in-a-haystack items (no RULER data is used).
+# The pages give no query length; both use a 512-token query block, which
+# makes the host blocks whole 64-key tiles (L = 3968 and 16064).
+QWEN3B_32K_PAGE_DEFAULTS = Workload("qwen2.5vl3b_32k_page_defaults", BF16, 16, 2, 128,
+                                    32768 // 64, 8, 3968, 512, 32768 // 128,
+                                    "planted_frac", 0.01, seed=5)
+LLAMA8B_128K_TEXT = Workload("llama3.1-8b_128k_text", BF16, 32, 8, 128,
+                             131072 // 64, 8, 16064, 512, 131072 // 128,
+                             "needle", 64, seed=6)
+# The same 32K re-split with a 128-token query block: host blocks of 4016
+# keys, not whole tiles.
+QWEN3B_32K_PAGE_DEFAULTS_Q128 = QWEN3B_32K_PAGE_DEFAULTS.with_(
+    name="qwen2.5vl3b_32k_page_defaults_q128", host_len=4016, n_query=128)
+PAGE_DEFAULT_WORKLOADS = [QWEN3B_32K_PAGE_DEFAULTS, LLAMA8B_128K_TEXT]
+
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even).
