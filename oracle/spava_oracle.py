@@ -96,6 +96,59 @@ def block_scores(q, k, la, V, L, n_q, scale=None):
     return out
 
 
+def context_block_scores(q, k, la, V, L, n_q, scale=None):
+    """Context-driven importance of every key of every block: the referee's
+    alternative selector.
+
+    [APB-V] Referee Report, major comment 1 (select the top-lp KVs of a block
+    by cumulative attention from all tokens in the context block, and compare
+    that selection with the query-based one) and "What would settle it" (the
+    overlap of the two selected sets).  Reading: every token t of block h and
+    every query head a of group g attends causally over the block's own keys
+    (j <= t, diagonal included), the softmax taken over those keys only;
+    score[j] sums these probabilities over the block's tokens and the group's
+    heads.  Selection then follows select_passing unchanged.
+
+    q: [N, Hq, d], k: [N, Hkv, d].  Returns float64 [V, Hkv, L].
+    """
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seg = split_sequence(la, V, L, n_q)
+    visible = np.tril(np.ones((L, L), dtype=bool))                  # token t sees keys j <= t
+    out = np.zeros((V, Hkv, L), dtype=np.float64)
+    for h, (b0, b1) in enumerate(seg["blocks"]):
+        for g in range(Hkv):
+            keys = np.asarray(k[b0:b1, g, :], dtype=np.float64)     # [L, d]
+            for a in range(g * G, (g + 1) * G):
+                rows = np.asarray(q[b0:b1, a, :], dtype=np.float64)  # the block's own tokens
+                s = np.where(visible, (rows @ keys.T) * scale, NEG_INF)
+                s = s - s.max(axis=1, keepdims=True)
+                p = np.exp(s)
+                p = p / p.sum(axis=1, keepdims=True)
+                out[h, g] += p.sum(axis=0)
+    return out
+
+
+def kv_overlap(idx_a, idx_b):
+    """Number of keys two selections share, per (block, KV head).
+
+    [APB-V] "What would settle it": the overlap between the query-selected
+    and the context-selected KV sets.  idx_*: [V, Hkv, lp].  Returns int64
+    [V, Hkv].
+    """
+    idx_a = np.asarray(idx_a)
+    idx_b = np.asarray(idx_b)
+    V, Hkv, _ = idx_a.shape
+    out = np.zeros((V, Hkv), dtype=np.int64)
+    for h in range(V):
+        for g in range(Hkv):
+            out[h, g] = len(set(idx_a[h, g].tolist()) & set(idx_b[h, g].tolist()))
+    return out
+
+
 def select_passing(scores, lp: int):
     """ArgTop_lp per (block, KV head), ties to the lower index, ascending.
 
