@@ -43,9 +43,14 @@ def attn_flops(w) -> float:
     return 4.0 * w.head_dim * w.n_q_heads * attn_pairs_per_head(w)
 
 
-def score_flops(w) -> float:
-    """One Q K^T pass of the query rows over every block (both score passes
-    recompute it; only one is counted as algorithmic work)."""
+def score_flops(w, selector="query") -> float:
+    """One Q K^T pass of the scoring rows over their keys (both score passes
+    recompute it; only one is counted as algorithmic work): the query rows
+    over every block, or (context selector) each block's tokens causally over
+    the block's own keys."""
+    if selector == "context":
+        L = w.host_len
+        return 2.0 * w.head_dim * w.n_q_heads * w.n_hosts * (L * (L + 1) // 2)
     return 2.0 * w.head_dim * (w.n_query * w.n_q_heads) * (w.n_hosts * w.host_len)
 
 
@@ -73,11 +78,13 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(w, x):
+def cpu_baseline(w, x, selector="query"):
     """The oracle as it stands, on a bounded sample of the same layer:
     scoring + selection in full, then the context rows of hosts 0 and V-1
     for the query heads of one KV group; the attention time is extrapolated
-    to the whole layer by its share of attention pairs."""
+    to the whole layer by its share of attention pairs.  With the context
+    selector the scoring is timed on block 0 and KV head 0 and extrapolated
+    to all V * Hkv lists."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -85,25 +92,34 @@ def cpu_baseline(w, x):
     except Exception:
         cores = os.cpu_count() or 1
     la, V, L, nq, lp = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.lp
+    scale = 1.0 / math.sqrt(w.head_dim)
+    G = w.group
     t0 = time.perf_counter()
-    sc = O.block_scores(x["q"], x["k"], la, V, L, nq)
+    t_extra = 0.0
+    if selector == "context":
+        sc = np.zeros((V, w.n_kv_heads, L))
+        sc[0, 0] = O.context_block_scores(x["q"][la:la + L, :G], x["k"][la:la + L, :1], 0, 1, L, 0, scale)[0, 0]
+        t_extra = (time.perf_counter() - t0) * (V * w.n_kv_heads - 1)
+    else:
+        sc = O.block_scores(x["q"], x["k"], la, V, L, nq)
     idx = O.select_passing(sc, lp)
     kp, vp = O.gather_passing(x["k"], x["v"], idx, la, L)
     t1 = time.perf_counter()
-    scale = 1.0 / math.sqrt(w.head_dim)
-    G = w.group
     for h in (0, V - 1):                    # the query heads of KV group 0
         O.context_rows(x["q"][:, :G], x["k"][:, :1], x["v"][:, :1], kp[:1], vp[:1], la, V, L, h, scale)
     t2 = time.perf_counter()
     sample_pairs = G * sum(L * (la + h * lp) + L * (L + 1) // 2 for h in (0, V - 1))
     total_pairs = attn_pairs_per_head(w) * w.n_q_heads
-    t_layer = (t1 - t0) + (t2 - t1) * total_pairs / sample_pairs
+    t_select = (t1 - t0) + t_extra
+    t_layer = t_select + (t2 - t1) * total_pairs / sample_pairs
     return {
         "value": w.n_tokens / t_layer,
         "unit": "tokens/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle: scores+top-lp+gather of the full layer ({t1 - t0:.1f} s), "
+        "sample": (f"float64 numpy oracle: {selector} scores+top-lp+gather of the full layer ({t_select:.1f} s"
+                   + (", context scores of one of the V*Hkv lists timed and extrapolated" if selector == "context" else "")
+                   + "), "
                    f"then context rows of hosts 0 and {V - 1} for {G} of {w.n_q_heads} query heads "
                    f"({t2 - t1:.1f} s); attention extrapolated by pair count "
                    f"({total_pairs / sample_pairs:.1f}x) to {t_layer:.1f} s per layer"),
@@ -117,6 +133,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    ap.add_argument("--selector", choices=("query", "context"), default="query",
+                    help="which rule scores the keys: the query block's attention (the pages' "
+                         "method) or each block's own tokens (the referee's alternative)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -138,13 +157,18 @@ def main():
     to = lambda n: torch.from_numpy(x[n + "16"].view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to("q"), to("k"), to("v")
     bufs = S.alloc_buffers(plan, dev)
+    if args.selector == "context":
+        score_topk = S.spava_score_topk_context
+        ws_score = torch.empty(max(256, S.spava_score_topk_context_ws_bytes(plan)), dtype=torch.uint8, device=dev)
+    else:
+        score_topk, ws_score = S.spava_score_topk, bufs.ws_score
     stream = torch.cuda.current_stream()
     q0 = wl.n_anchor + wl.n_hosts * wl.host_len
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        S.spava_score_topk(plan, q, k, bufs.scores, bufs.idx, bufs.ws_score, stream)
+        score_topk(plan, q, k, bufs.scores, bufs.idx, ws_score, stream)
         if ev is not None:
             ev[1].record(stream)
         S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
@@ -205,16 +229,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.n_tokens, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "anchor": wl.n_anchor,
-                   "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp},
+                   "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp,
+                   "selector": args.selector},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(wl.name)},
         "attn_tflop_per_launch": F_attn / 1e12,
-        "step_tflops": (F_attn + score_flops(wl)) / (ms_per_step * 1e-3) / 1e12,
+        "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,
+        "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
         "stage_ms": stage_ms,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, x)
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.selector)
     print(json.dumps(out), flush=True)
 
 

@@ -12,6 +12,9 @@
  *                            block's attention and keep the top lp per block
  *                            and KV head (Figure 5 caption; review "What
  *                            carries the argument"; ledger axiom on ArgTop_lp)
+ *      spava_score_topk_context  the same with the block's own tokens as the
+ *                            scorers (review, Referee Report, major comment
+ *                            1); spava_kv_overlap compares two selections
  *   2. spava_gather_passing  copy the kept K,V rows into passing blocks
  *                            (Figure 2 caption: blocks compressed, then passed)
  *   3. spava_attn_fwd        anchor and context tokens attend over anchor +
@@ -123,6 +126,46 @@ size_t spava_score_topk_ws_bytes(const spava_plan* plan);
 int spava_score_topk(const spava_plan* plan, const void* q, const void* k,
                      float* scores, int32_t* idx, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * Workspace bytes spava_score_topk_context needs: as spava_score_topk_ws_bytes
+ * with the block's L tokens as the scoring rows, float32 [V][Hkv][L*G] for
+ * float32 plans and float32 [C][V][Hkv][L*G][2] for bf16 plans.
+ */
+size_t spava_score_topk_context_ws_bytes(const spava_plan* plan);
+
+/*
+ * Context-driven selection: the alternative the APB-V review's Referee
+ * Report (major comment 1) asks to compare against -- a block's own tokens,
+ * not the query block, decide which of its keys are passed on.  For block h
+ * and KV head g,
+ *     scores[h][g][j] = sum over block tokens t >= j and query heads a of
+ *                       group g of softmax_{j' <= t}( q[la+h*L+t][a] .
+ *                       k[la+h*L+j'][g] * scale )
+ * i.e. every token attends causally over its own block (diagonal included)
+ * and the probabilities it gives each key are summed.  Selection, layouts,
+ * alignment and errors as spava_score_topk; ws >=
+ * spava_score_topk_context_ws_bytes(plan).  L * (n_q_heads / n_kv_heads)
+ * must be below 2^31.  Costs about one causal attention pass per block
+ * (two MFMA passes over its L x L logits), against the L x n_q logits of the
+ * query-driven rule.
+ */
+int spava_score_topk_context(const spava_plan* plan, const void* q,
+                             const void* k, float* scores, int32_t* idx,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Overlap of two selections (APB-V review, "What would settle it": how many
+ * of the query-selected keys the context-driven rule also selects).
+ *   idx_a, idx_b  [n_lists][lp] int32, each list strictly ascending (as
+ *                 spava_score_topk and spava_score_topk_context write them)
+ *   counts        [n_lists] int32, written: |a_i intersect b_i|, or -1 for
+ *                 a list pair where either list is not strictly ascending
+ * n_lists = V * Hkv for the outputs of the two selectors.  Pointers are
+ * device pointers, 4-byte aligned; n_lists * lp must be below 2^31.
+ */
+int spava_kv_overlap(int32_t n_lists, int32_t lp, const int32_t* idx_a,
+                     const int32_t* idx_b, int32_t* counts, void* stream);
 
 /*
  * Step 2: passing blocks (Figure 2 caption).

@@ -25,7 +25,8 @@ SPAVA_OK, SPAVA_EINVAL, SPAVA_EUNSUPPORTED, SPAVA_EWORKSPACE, SPAVA_ELAUNCH = ra
 SPAVA_BF16, SPAVA_F32 = 0, 1
 EXPORTS = ("spava_version", "spava_last_error", "spava_plan_check", "spava_score_topk_ws_bytes",
            "spava_score_topk", "spava_gather_passing", "spava_attn_fwd_ws_bytes", "spava_attn_fwd",
-           "spava_lse_merge")
+           "spava_lse_merge", "spava_score_topk_context_ws_bytes", "spava_score_topk_context",
+           "spava_kv_overlap")
 
 
 class SpavaError(RuntimeError):
@@ -61,6 +62,10 @@ def lib():
         L.spava_score_topk_ws_bytes.argtypes = [P]
         L.spava_score_topk_ws_bytes.restype = sz
         L.spava_score_topk.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_score_topk_context_ws_bytes.argtypes = [P]
+        L.spava_score_topk_context_ws_bytes.restype = sz
+        L.spava_score_topk_context.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_kv_overlap.argtypes = [i32, i32, vp, vp, vp, vp]
         L.spava_gather_passing.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.spava_attn_fwd_ws_bytes.argtypes = [P]
         L.spava_attn_fwd_ws_bytes.restype = sz
@@ -134,6 +139,10 @@ def spava_score_topk_ws_bytes(plan: Plan) -> int:
     return lib().spava_score_topk_ws_bytes(ctypes.byref(plan.c()))
 
 
+def spava_score_topk_context_ws_bytes(plan: Plan) -> int:
+    return lib().spava_score_topk_context_ws_bytes(ctypes.byref(plan.c()))
+
+
 def spava_attn_fwd_ws_bytes(plan: Plan) -> int:
     return lib().spava_attn_fwd_ws_bytes(ctypes.byref(plan.c()))
 
@@ -146,6 +155,31 @@ def spava_score_topk(plan: Plan, q, k, scores, idx, ws, stream=None):
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
     _check(lib().spava_score_topk(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spava_score_topk_context(plan: Plan, q, k, scores, idx, ws, stream=None):
+    """Context-driven selection: the block's own tokens score its keys."""
+    p = plan
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
+    _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
+    _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
+    _check(lib().spava_score_topk_context(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spava_kv_overlap(idx_a, idx_b, counts, stream=None):
+    """idx_a, idx_b [..., lp] int32 (strictly ascending lists); counts [...]
+    int32 receives the size of each pair's intersection (-1 if a list is not
+    strictly ascending)."""
+    if tuple(idx_a.shape) != tuple(idx_b.shape) or idx_a.dim() < 1:
+        raise ValueError("idx_a and idx_b must have the same shape [..., lp]")
+    lp = idx_a.shape[-1]
+    _expect(idx_a, idx_a.shape, torch.int32, "idx_a")
+    _expect(idx_b, idx_b.shape, torch.int32, "idx_b")
+    _expect(counts, idx_a.shape[:-1], torch.int32, "counts")
+    _check(lib().spava_kv_overlap(counts.numel(), lp, _ptr(idx_a), _ptr(idx_b), _ptr(counts),
+                                  _stream(stream)))
 
 
 def spava_gather_passing(plan: Plan, k, v, idx, kp, vp, stream=None):

@@ -75,14 +75,58 @@ AttnArgs make_args(const spava_plan* p) {
 }
 
 // Scoring workspace: float32 inputs keep one log2-domain LSE per (block, KV
-// head, query row); bf16 inputs keep a (max, sum) pair per key chunk.
-size_t stats_bytes(const spava_plan* p) {
-  const size_t R = (size_t)p->n_query * (p->n_q_heads / p->n_kv_heads);
+// head, scoring row); bf16 inputs keep a (max, sum) pair per key chunk.  The
+// query selector's rows are the query block's tokens, the context selector's
+// the block's own tokens (each times the G heads of a group).
+size_t stats_bytes(const spava_plan* p, bool ctx) {
+  const size_t ntok = ctx ? (size_t)p->host_len : (size_t)p->n_query;
+  const size_t R = ntok * (p->n_q_heads / p->n_kv_heads);
   const size_t rows = (size_t)p->n_hosts * p->n_kv_heads * R;
   const size_t bytes = p->dtype == SPAVA_F32
                            ? rows * sizeof(float)
                            : rows * (size_t)score_bf16_key_chunks(p->host_len) * sizeof(float2);
   return (bytes + 255) / 256 * 256;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPAVA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SPAVA_OK;
+}
+
+// Block scores and top-lp selection with the query rows (ctx = false) or the
+// block's own tokens (ctx = true) as the scoring rows.
+int score_topk(const char* name, bool ctx, const spava_plan* plan, const void* q, const void* k,
+               float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  if (!q || !k || !scores || !ws || (plan->lp > 0 && !idx))
+    return fail(SPAVA_EINVAL, "%s: q, k, scores, ws (and idx when lp > 0) must be non-NULL", name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) || (idx && !aligned16(idx)))
+    return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
+  const size_t need = stats_bytes(plan, ctx);
+  if (ws_bytes < need) return fail(SPAVA_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  if (ctx && (double)plan->host_len * (plan->n_q_heads / plan->n_kv_heads) >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "%s: host_len * (n_q_heads / n_kv_heads) must stay below 2^31", name);
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a = make_args(plan);
+  a.q = q;
+  a.k = k;
+  a.score_ctx = ctx ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (a.f32) {
+    a.stats = (float*)ws;
+    if (score_rows(a, 0).R > 0) {
+      e = launch_rowstat_f32(a, s);
+      if (e != hipSuccess) return launched(e, "row statistics");
+    }
+    e = launch_colsum_f32(a, scores, s);
+  } else {
+    e = launch_score_bf16(a, (float2*)ws, scores, s);
+  }
+  if (e != hipSuccess) return launched(e, "block scores");
+  e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);
+  return launched(e, "top-lp selection");
 }
 
 size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
@@ -94,11 +138,6 @@ size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
   return main_al + (pass + 255) / 256 * 256;
 }
 
-int launched(hipError_t e, const char* what) {
-  if (e != hipSuccess) return fail(SPAVA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
-  g_err[0] = 0;
-  return SPAVA_OK;
-}
 
 }  // namespace
 }  // namespace spava
@@ -119,37 +158,38 @@ int spava_plan_check(const spava_plan* plan) {
 
 size_t spava_score_topk_ws_bytes(const spava_plan* plan) {
   if (check_plan(plan) != SPAVA_OK) return 0;
-  return stats_bytes(plan);
+  return stats_bytes(plan, false);
 }
 
 int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float* scores,
                      int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_plan(plan);
-  if (rc) return rc;
-  if (!q || !k || !scores || !ws || (plan->lp > 0 && !idx))
-    return fail(SPAVA_EINVAL, "spava_score_topk: q, k, scores, ws (and idx when lp > 0) must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) || (idx && !aligned16(idx)))
-    return fail(SPAVA_EINVAL, "spava_score_topk: pointers must be 16-byte aligned");
-  if (ws_bytes < stats_bytes(plan))
-    return fail(SPAVA_EWORKSPACE, "spava_score_topk: workspace %zu < %zu bytes", ws_bytes, stats_bytes(plan));
-  hipStream_t s = (hipStream_t)stream;
-  AttnArgs a = make_args(plan);
-  a.q = q;
-  a.k = k;
-  hipError_t e = hipSuccess;
-  if (a.f32) {
-    a.stats = (float*)ws;
-    if (a.nq > 0) {
-      e = launch_rowstat_f32(a, s);
-      if (e != hipSuccess) return launched(e, "row statistics");
-    }
-    e = launch_colsum_f32(a, scores, s);
-  } else {
-    e = launch_score_bf16(a, (float2*)ws, scores, s);
+  return score_topk("spava_score_topk", false, plan, q, k, scores, idx, ws, ws_bytes, stream);
+}
+
+size_t spava_score_topk_context_ws_bytes(const spava_plan* plan) {
+  if (check_plan(plan) != SPAVA_OK) return 0;
+  return stats_bytes(plan, true);
+}
+
+int spava_score_topk_context(const spava_plan* plan, const void* q, const void* k, float* scores,
+                             int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return score_topk("spava_score_topk_context", true, plan, q, k, scores, idx, ws, ws_bytes, stream);
+}
+
+int spava_kv_overlap(int32_t n_lists, int32_t lp, const int32_t* idx_a, const int32_t* idx_b,
+                     int32_t* counts, void* stream) {
+  if (n_lists < 0 || lp < 0) return fail(SPAVA_EINVAL, "spava_kv_overlap: need n_lists >= 0 and lp >= 0");
+  if (n_lists == 0) {
+    g_err[0] = 0;
+    return SPAVA_OK;
   }
-  if (e != hipSuccess) return launched(e, "block scores");
-  e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);
-  return launched(e, "top-lp selection");
+  if (!counts || (lp > 0 && (!idx_a || !idx_b)))
+    return fail(SPAVA_EINVAL, "spava_kv_overlap: NULL pointer");
+  if (((uintptr_t)counts | (uintptr_t)idx_a | (uintptr_t)idx_b) & 3u)
+    return fail(SPAVA_EINVAL, "spava_kv_overlap: pointers must be 4-byte aligned");
+  if ((double)n_lists * lp >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "spava_kv_overlap: n_lists * lp must stay below 2^31");
+  return launched(launch_overlap(idx_a, idx_b, counts, n_lists, lp, (hipStream_t)stream), "overlap");
 }
 
 int spava_gather_passing(const spava_plan* plan, const void* k, const void* v, const int32_t* idx,

@@ -11,6 +11,11 @@
 // accumulate in float64 in a fixed order, so the result is deterministic and
 // its relative error stays far below 1e-6.
 //
+// With AttnArgs::score_ctx set the rows are block h's own tokens instead (the
+// context-driven selector of the APB-V review's Referee Report, major comment
+// 1), each attending causally over the block's keys: key j counts for token t
+// iff j <= t.
+//
 // Selection (ArgTop_lp in the APB-V review's axiom ledger): an exact radix
 // select on the order-preserving integer image of the float32 scores finds
 // the lp-th largest value; ties at that value go to the lower indices; the
@@ -23,14 +28,16 @@ namespace {
 // float32 inputs: row statistics and column sums on the vector ALUs.
 template <int D>
 __global__ __launch_bounds__(256) void rowstat_f32_kernel(AttnArgs a) {
-  const int R = a.nq * a.G;
+  const int R = score_rows(a, 0).R;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)a.V * a.Hkv * R) return;
   const int r = (int)(gid % R);
   const int hg = (int)(gid / R);
   const int h = hg / a.Hkv, g = hg % a.Hkv;
-  const int tok = a.la + a.V * a.L + r % a.nq;
-  const int head = g * a.G + r / a.nq;
+  const ScoreRows sr = score_rows(a, h);
+  const int tok = sr.tok0 + r % sr.ntok;
+  const int head = g * a.G + r / sr.ntok;
+  const int nkeys = a.score_ctx ? r % sr.ntok + 1 : a.L;   // keys [0, nkeys) are visible
   const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
   float qv[D];
 #pragma unroll
@@ -38,7 +45,7 @@ __global__ __launch_bounds__(256) void rowstat_f32_kernel(AttnArgs a) {
   const long kstr = (long)a.Hkv * D;
   const float* kb = (const float*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
   float m = -INFINITY, l = 0.0f;
-  for (int j = 0; j < a.L; ++j) {
+  for (int j = 0; j < nkeys; ++j) {
     const float* kr = kb + (long)j * kstr;
     float s = 0.0f;
 #pragma unroll
@@ -53,12 +60,13 @@ __global__ __launch_bounds__(256) void rowstat_f32_kernel(AttnArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __restrict__ scores) {
-  const int R = a.nq * a.G;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)a.V * a.Hkv * a.L) return;
   const int j = (int)(gid % a.L);
   const int hg = (int)(gid / a.L);
   const int h = hg / a.Hkv, g = hg % a.Hkv;
+  const ScoreRows sr = score_rows(a, h);
+  const int R = sr.R;
   const long kstr = (long)a.Hkv * D;
   const float* kr = (const float*)a.k + (long)(a.la + h * a.L + j) * kstr + (long)g * D;
   float kv[D];
@@ -67,8 +75,9 @@ __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __re
   const float* lse2 = a.stats + (long)hg * R;
   double acc = 0.0;
   for (int r = 0; r < R; ++r) {
-    const int tok = a.la + a.V * a.L + r % a.nq;
-    const int head = g * a.G + r / a.nq;
+    if (a.score_ctx && r % sr.ntok < j) continue;   // token r % L does not see key j
+    const int tok = sr.tok0 + r % sr.ntok;
+    const int head = g * a.G + r / sr.ntok;
     const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
     float s = 0.0f;
 #pragma unroll
@@ -211,10 +220,66 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Overlap of two selections ("What would settle it" in the APB-V review: how
+// many of the keys kept by the query-driven rule the context-driven rule also
+// keeps).  One workgroup per list pair; every entry of list a is looked up in
+// list b by binary search.  Both lists must be strictly ascending (as the
+// top-lp selection writes them); a pair where either is not gets -1.
+// ---------------------------------------------------------------------------
+constexpr int kOverlapThreads = 256;
+
+__global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(const int32_t* __restrict__ idx_a,
+                                                                  const int32_t* __restrict__ idx_b,
+                                                                  int32_t* __restrict__ counts, int lp) {
+  __shared__ int sCount[kOverlapThreads / 64];
+  __shared__ int sBad[kOverlapThreads / 64];
+  const int tid = threadIdx.x;
+  const int32_t* A = idx_a + (long)blockIdx.x * lp;
+  const int32_t* B = idx_b + (long)blockIdx.x * lp;
+  int n = 0, bad = 0;
+  for (int i = tid; i < lp; i += kOverlapThreads) {
+    if (i + 1 < lp) bad |= (A[i] >= A[i + 1]) | (B[i] >= B[i + 1]);
+    const int x = A[i];
+    int lo = 0, hi = lp;               // first position in B whose value is >= x
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (B[mid] < x) lo = mid + 1;
+      else hi = mid;
+    }
+    n += (lo < lp && B[lo] == x);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n += __shfl_xor(n, o);
+    bad |= __shfl_xor(bad, o);
+  }
+  if ((tid & 63) == 0) {
+    sCount[tid >> 6] = n;
+    sBad[tid >> 6] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0, any_bad = 0;
+    for (int w = 0; w < kOverlapThreads / 64; ++w) {
+      tot += sCount[w];
+      any_bad |= sBad[w];
+    }
+    counts[blockIdx.x] = any_bad ? -1 : tot;
+  }
+}
+
 }  // namespace
 
+hipError_t launch_overlap(const int32_t* idx_a, const int32_t* idx_b, int32_t* counts, int n_lists, int lp,
+                          hipStream_t s) {
+  if (n_lists == 0) return hipSuccess;
+  hipLaunchKernelGGL(overlap_kernel, dim3(n_lists), dim3(kOverlapThreads), 0, s, idx_a, idx_b, counts, lp);
+  return hipGetLastError();
+}
+
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s) {
-  const long nr = (long)a.V * a.Hkv * a.nq * a.G;
+  const long nr = (long)a.V * a.Hkv * score_rows(a, 0).R;
   if (nr == 0) return hipSuccess;
   const dim3 grid((unsigned)((nr + 255) / 256));
   if (a.D == 128)
@@ -224,12 +289,12 @@ hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Column sums; a.stats must already hold the row statistics.  With an empty
-// query block every score is 0 (a sum over no rows).
+// Column sums; a.stats must already hold the row statistics.  With no
+// scoring rows (an empty query block) every score is 0 (a sum over no rows).
 hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s) {
   const long n = (long)a.V * a.Hkv * a.L;
   if (n == 0) return hipSuccess;
-  if (a.nq * a.G == 0) {
+  if (score_rows(a, 0).R == 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, scores, n);
     return hipGetLastError();
   }

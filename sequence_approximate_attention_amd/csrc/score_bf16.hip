@@ -15,6 +15,12 @@
 //     ahead.  Splitting the block into chunks gives the GPU enough
 //     workgroups; the partial (max, sum) pairs are combined by the next pass.
 //
+// CTX = true gives the context-driven selector (APB-V review, Referee Report,
+// major comment 1): the rows are block h's own tokens, each attending
+// causally over the block's keys (key j visible to token t iff j <= t); key
+// chunks above a workgroup's last token and row chunks below its first key
+// are skipped.
+//
 //   colsum_kernel: combines each row's chunk partials into its log2-domain
 //     log-sum-exp, then for 256 keys per workgroup sums exp2(s - lse) over all
 //     rows.  Each wave keeps 64 keys' fragments in registers; the two halves
@@ -49,11 +55,17 @@ struct RsGeo {
   static constexpr int KINST = KBYTES / 1024 / kRsWaves;
 };
 
-// Query row r of group g: token q0 + r % nq, head g * G + r / nq.
-__device__ __forceinline__ long q_row_elem(const AttnArgs& a, int g, int r) {
-  const int tok = a.la + a.V * a.L + r % a.nq;
-  const int head = g * a.G + r / a.nq;
+// Element offset of scoring row r of KV head g (see score_rows).
+__device__ __forceinline__ long q_row_elem(const AttnArgs& a, const ScoreRows& sr, int g, int r) {
+  const int tok = sr.tok0 + r % sr.ntok;
+  const int head = g * a.G + r / sr.ntok;
   return ((long)tok * a.Hq + head) * a.D;
+}
+
+// Largest block-local token among the rows [r_lo, r_hi] (inclusive) of the
+// context selector's row order.
+__device__ __forceinline__ int last_token(int r_lo, int r_hi, int ntok) {
+  return (r_lo / ntok != r_hi / ntok) ? ntok - 1 : r_hi % ntok;
 }
 
 // This wave's share of the copy of tile t of the chunk into kbuf.  Every lane
@@ -79,7 +91,7 @@ __device__ __forceinline__ void rs_issue(const u32x4& rs_blk, int kstride2, int 
   }
 }
 
-template <int D>
+template <int D, bool CTX>
 __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a, int KC, int TPC, int RT,
                                                                        float2* __restrict__ part) {
   using G = RsGeo<D>;
@@ -92,7 +104,6 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
   const int col = lane & 31;
-  const int R = a.nq * a.G;
   const int VH = a.V * a.Hkv;
 
   // Unit b = ((h * Hkv + g) * KC + kc) * RT + rt: the row tiles of one key
@@ -105,15 +116,17 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   const int hg = b / (RT * KC);
   const int h = hg / a.Hkv;
   const int g = hg % a.Hkv;
+  const ScoreRows sr = score_rows(a, h);
+  const int R = sr.R;
 
-  // This lane's two query rows (one per 32-column block).
+  // This lane's two scoring rows (one per 32-column block).
   int r[2];
   bf16x8 qf[2][NC];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     r[qb] = rt * kRsBM + wave * kRsWaveRows + 32 * qb + col;
     const bool valid = r[qb] < R;
-    const uint16_t* qp = (const uint16_t*)a.q + q_row_elem(a, g, valid ? r[qb] : 0) + 8 * hi;
+    const uint16_t* qp = (const uint16_t*)a.q + q_row_elem(a, sr, g, valid ? r[qb] : 0) + 8 * hi;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qf[qb][c] = *(const bf16x8*)(qp + 16 * c);
@@ -128,7 +141,16 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   // are masked.
   const int T = ceil_div(a.L, kBN);
   const int t0 = kc * TPC;
-  const int nt = min(T, t0 + TPC) - t0;
+  int nt = min(T, t0 + TPC) - t0;
+  int lim_row[2] = {a.L, a.L};   // block-local keys visible to this lane's rows: [0, lim_row)
+  if (CTX) {
+    // Tiles past the workgroup's last token hold no visible key.
+    const int r_lo = rt * kRsBM;
+    const int r_hi = min(R, r_lo + kRsBM) - 1;
+    nt = max(0, min(nt, ceil_div(last_token(r_lo, r_hi, sr.ntok) + 1, kBN) - t0));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) lim_row[qb] = (r[qb] < R) ? r[qb] % sr.ntok + 1 : 0;
+  }
   const int kstride2 = a.Hkv * D * 2;
   const uint16_t* kblk = (const uint16_t*)a.k + ((long)(a.la + h * a.L) * a.Hkv + g) * D;
   const u32x4 rs_blk = make_rsrc(kblk, (unsigned)a.L * (unsigned)kstride2);
@@ -164,8 +186,12 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
         for (int qb = 0; qb < 2; ++qb)
           s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][c], c == 0 ? f32x16{} : s[qb][h2], 0, 0, 0);
       }
-    const int lim = a.L - (t0 + t) * kBN;   // tile-local key j is in the block iff j < lim
-    if (lim < kBN) {
+    // Tile-local key j is visible to a row iff j < lim (past the block's end,
+    // and for the context selector past the row's own token, it is masked).
+    int lim[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) lim[qb] = min(a.L, lim_row[qb]) - (t0 + t) * kBN;
+    if (__any(lim[0] < kBN || lim[1] < kBN)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int j = 32 * h2 + (e & 7) + 8 * hi + 16 * (e >> 3);
-            if (j >= lim) s[qb][h2][e] = -INFINITY;
+            if (j >= lim[qb]) s[qb][h2][e] = -INFINITY;
           }
     }
 #pragma unroll
@@ -227,25 +253,26 @@ struct CsGeo {
   static constexpr int QINST = QBYTES / 1024 / kCsWavesPerHalf;
 };
 
-// This wave's share of the copy of the Q rows [r0, r0 + 32) into qbuf.  Row r
-// is token r % nq of head g * G + r / nq (one division per chunk, then each
-// lane steps from r0); rows at or past R read row 0, a real row whose
-// probabilities the +inf LSE of those rows zeroes.
+// This wave's share of the copy of the scoring rows [r0, r0 + 32) into qbuf
+// (rs_q covers the rows' tokens from tok0 on).  Row r is token r % ntok of
+// head g * G + r / ntok (one division per chunk, then each lane steps from
+// r0); rows at or past R read row 0, a real row whose probabilities the +inf
+// LSE of those rows zeroes.
 template <int D>
-__device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, int g, int r0, int R,
+__device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, int ntok, int g, int r0, int R,
                                          char* qbuf, int w4, int lane) {
   using G = CsGeo<D>;
   const int q = lane / (G::QRB / 16);
   const int slot = lane % (G::QRB / 16);
-  const int i0 = r0 % a.nq;
-  const int a0 = r0 / a.nq;
+  const int i0 = r0 % ntok;
+  const int a0 = r0 / ntok;
 #pragma unroll
   for (int j = 0; j < G::QINST; ++j) {
     const int blk = w4 * G::QINST + j;
     const int row = blk * G::RPI + q;   // row within the chunk
     int tok = i0 + row, head = a0;
-    while (tok >= a.nq) {               // at most 32 / nq + 1 steps
-      tok -= a.nq;
+    while (tok >= ntok) {               // at most 32 / ntok + 1 steps
+      tok -= ntok;
       ++head;
     }
     if (r0 + row >= R) {
@@ -258,7 +285,7 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
   }
 }
 
-template <int D>
+template <int D, bool CTX>
 __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int KC,
                                                                const float2* __restrict__ part,
                                                                float* __restrict__ scores) {
@@ -279,7 +306,8 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   const int hg = blockIdx.y;   // h * Hkv + g
   const int h = hg / a.Hkv;
   const int g = hg % a.Hkv;
-  const int R = a.nq * a.G;
+  const ScoreRows sr = score_rows(a, h);
+  const int R = sr.R;
   const int VH = a.V * a.Hkv;
   const long kstr = (long)a.Hkv * D;
   const int key0 = blockIdx.x * kCsKeys + w4 * 64;
@@ -296,8 +324,8 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   }
   wait_vm<0>();   // as in the row statistics: no compiler wait inside the chunk loop
 
-  const u32x4 rs_q = make_rsrc((const uint16_t*)a.q + (long)(a.la + a.V * a.L) * a.Hq * D,
-                               (unsigned)a.nq * (unsigned)a.Hq * (unsigned)D * 2u);
+  const u32x4 rs_q = make_rsrc((const uint16_t*)a.q + (long)sr.tok0 * a.Hq * D,
+                               (unsigned)sr.ntok * (unsigned)a.Hq * (unsigned)D * 2u);
   char* const myq = sQ + half * kCsSlots * G::QBYTES;
   const float sl2 = a.scale_log2;
   double acc[2] = {0.0, 0.0};
@@ -311,7 +339,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
 #pragma unroll
     for (int j = 0; j < kCsSlots - 1; ++j) {
       const int c = kCsHalves * j + half;
-      cs_issue<D>(a, rs_q, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
+      cs_issue<D>(a, rs_q, sr.ntok, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
     }
     // ... while the row LSEs are combined from the chunk partials:
     // lse = M + log2(sum_k l_k 2^(m_k - M)); rows past R get +inf (weight 0).
@@ -341,11 +369,21 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
       {
         const int jn = j + kCsSlots - 1;
         const int cn = kCsHalves * jn + half;
-        cs_issue<D>(a, rs_q, g, (jn < nj && cn < nch) ? rb + cn * kCsRows : R, R,
+        cs_issue<D>(a, rs_q, sr.ntok, g, (jn < nj && cn < nch) ? rb + cn * kCsRows : R, R,
                     myq + (jn % kCsSlots) * G::QBYTES, w4, lane);
       }
       const int c = kCsHalves * j + half;
       if (c >= nch) continue;
+      // Context selector: the chunk's tokens t see keys j <= t only.
+      const int r_lo = rb + c * kCsRows;
+      int t_first = 0;           // block-local token of the chunk's first row
+      bool need_mask = false;
+      if (CTX) {
+        const int r_hi = min(R, r_lo + kCsRows) - 1;
+        if (last_token(r_lo, r_hi, sr.ntok) < key0) continue;   // none of this wave's keys is visible
+        t_first = r_lo % sr.ntok;
+        need_mask = (r_lo / sr.ntok != r_hi / sr.ntok) || t_first < key0 + 63;
+      }
       const char* qt = myq + (j % kCsSlots) * G::QBYTES;
       // LSE of this lane's accumulator rows m = 8 * (i / 4) + 4 * hi + i % 4.
       f32x4 lz[4];
@@ -360,8 +398,19 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][c16], c16 == 0 ? f32x16{} : s, 0, 0, 0);
         }
         float pz = 0.0f;
+        if (need_mask) {
+          const int jk = key0 + 32 * kb + col;     // this lane's key
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pz += __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lz[i >> 2][i & 3]));
+          for (int i = 0; i < 16; ++i) {
+            int t = t_first + 8 * (i >> 2) + 4 * hi + (i & 3);
+            while (t >= sr.ntok) t -= sr.ntok;     // rows of the next head restart at token 0
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lz[i >> 2][i & 3]));
+            pz += (jk <= t) ? p : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pz += __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lz[i >> 2][i & 3]));
+        }
         acc[kb] += (double)pz;
       }
     }
@@ -399,8 +448,9 @@ int score_bf16_tiles_per_chunk(int L) {
 }
 int score_bf16_key_chunks(int L) { return ceil_div(ceil_div(L, kBN), score_bf16_tiles_per_chunk(L)); }
 
-hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
-  const int R = a.nq * a.G;
+template <bool CTX>
+hipError_t launch_score_bf16_mode(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
+  const int R = score_rows(a, 0).R;
   const int VH = a.V * a.Hkv;
   const int KC = score_bf16_key_chunks(a.L);
   const int TPC = score_bf16_tiles_per_chunk(a.L);
@@ -409,18 +459,23 @@ hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hip
     const int n = VH * KC * RT;
     const dim3 grid(xcd_grid(n, RT));
     if (a.D == 128)
-      hipLaunchKernelGGL((rowstat_chunk_kernel<128>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
+      hipLaunchKernelGGL((rowstat_chunk_kernel<128, CTX>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
     else
-      hipLaunchKernelGGL((rowstat_chunk_kernel<64>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
+      hipLaunchKernelGGL((rowstat_chunk_kernel<64, CTX>), grid, dim3(kRsThreads), 0, s, a, KC, TPC, RT, part);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid(ceil_div(a.L, kCsKeys), VH);
   if (a.D == 128)
-    hipLaunchKernelGGL((colsum_kernel<128>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+    hipLaunchKernelGGL((colsum_kernel<128, CTX>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
   else
-    hipLaunchKernelGGL((colsum_kernel<64>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+    hipLaunchKernelGGL((colsum_kernel<64, CTX>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
   return hipGetLastError();
+}
+
+hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
+  return a.score_ctx ? launch_score_bf16_mode<true>(a, part, scores, s)
+                     : launch_score_bf16_mode<false>(a, part, scores, s);
 }
 
 }  // namespace spava

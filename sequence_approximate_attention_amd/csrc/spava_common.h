@@ -79,6 +79,7 @@ struct AttnArgs {
   int n_anchor_units;        // ceil(la/BM) * Hq
   int rows_per_unit;         // BM
   int f32;                   // 1: float32 elements, 0: bf16
+  int score_ctx;             // scoring rows: 0 = the query block, 1 = each block's own tokens
   int xcd_chunk;             // units per XCD chunk (see xcd_unit)
 };
 
@@ -251,6 +252,21 @@ __device__ inline RowId unit_row(const AttnArgs& a, const Unit& u, int r) {
   return x;
 }
 
+// Rows of the block scoring for block h: the query block's tokens (query
+// selector) or block h's own tokens, each attending causally over the
+// block's keys (context selector).  Row r of KV head g is token
+// tok0 + r % ntok of query head g * G + r / ntok; R = ntok * G rows.
+struct ScoreRows {
+  int tok0, ntok, R;
+};
+__host__ __device__ inline ScoreRows score_rows(const AttnArgs& a, int h) {
+  ScoreRows s;
+  s.tok0 = a.score_ctx ? a.la + h * a.L : a.la + a.V * a.L;
+  s.ntok = a.score_ctx ? a.L : a.nq;
+  s.R = s.ntok * a.G;
+  return s;
+}
+
 // ---- launchers (host), defined in the .hip files ----
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
@@ -263,6 +279,8 @@ hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hip
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);
+hipError_t launch_overlap(const int32_t* idx_a, const int32_t* idx_b, int32_t* counts, int n_lists,
+                          int lp, hipStream_t s);
 hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
                          int la, int V, int L, int Hkv, int lp, int row_bytes, hipStream_t s);
 hipError_t launch_merge(int P, int R, int H, int D, const float* o_part, const float* lse_part,

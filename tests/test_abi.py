@@ -68,6 +68,12 @@ def test_workspace_sizes():
     # float32 scoring: one log-sum-exp float per (block, KV head, query row), 256-byte rounded
     assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 16 * 2 * 4
     assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=3)) == 256
+    # context selector: the block's L tokens (times G heads) are the scoring rows
+    assert S.spava_score_topk_context_ws_bytes(p) == 1 * 4 * 1 * 128 * 2 * 8
+    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16)) == 2 * 4 * 1 * 1000 * 2 * 8
+    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4
+    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4
+    assert S.spava_score_topk_context_ws_bytes(plan(lp=999)) == 0
     # key-contiguous V: Hkv * d * (pad(la) + V*pad(L) + pad(n_q)) + passing, bf16
     main = 1 * 128 * (64 + 4 * 128 + 64) * 2
     pas = 1 * 128 * 64 * 2
@@ -98,3 +104,16 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     assert lib.spava_lse_merge(2, 0, 2, 64, None, None, None, 128, None, 0, S.SPAVA_F32, None) == S.SPAVA_OK
     p0 = plan(lp=0).c()
     assert lib.spava_gather_passing(ctypes.byref(p0), None, None, None, None, None, None) == S.SPAVA_OK
+    # Context selector: same checks as the query selector, its own workspace size.
+    assert lib.spava_score_topk_context(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert lib.spava_score_topk_context(ctypes.byref(p), odd, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    need = lib.spava_score_topk_context_ws_bytes(ctypes.byref(p))
+    assert lib.spava_score_topk_context(ctypes.byref(p), fake, fake, fake, fake, fake, need - 1, None) == S.SPAVA_EWORKSPACE
+    assert b"spava_score_topk_context" in lib.spava_last_error()
+    # Overlap: bad sizes, NULL or misaligned pointers; nothing to do succeeds.
+    assert lib.spava_kv_overlap(-1, 4, fake, fake, fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_kv_overlap(2, -4, fake, fake, fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_kv_overlap(2, 4, None, fake, fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_kv_overlap(2, 4, fake, fake, None, None) == S.SPAVA_EINVAL
+    assert lib.spava_kv_overlap(2, 4, fake, ctypes.c_void_p(0x10002), fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_kv_overlap(0, 4, None, None, None, None) == S.SPAVA_OK

@@ -151,12 +151,19 @@ def attention_copies(w, D, past_walk="stay"):
     return tiles
 
 
-def score_copies(w, D):
-    """Row statistics: K tiles of each key chunk; column sums: Q rows of each chunk."""
+RS_ROWS = 256    # rows per row-statistics workgroup
+
+
+def score_copies(w, D, ctx=False):
+    """Row statistics: K tiles of each key chunk; column sums: Q rows of each
+    chunk.  ctx=True walks the context selector: the scoring rows are each
+    block's own tokens, and a row-statistics workgroup stops at the tile of
+    its last token (possibly before its chunk's first tile)."""
     la, V, L, nq, Hq, Hkv = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.n_q_heads, w.n_kv_heads
     G = Hq // Hkv
     N = la + V * L + nq
-    R = nq * G
+    ntok = L if ctx else nq
+    R = ntok * G
     k = Extent("k", N * Hkv * D * 2)
     q = Extent("q", N * Hq * D * 2)
     if R == 0:
@@ -171,21 +178,32 @@ def score_copies(w, D):
             kblk = ((la + h * L) * Hkv + g) * D * 2
             for kc in range(kc_n):
                 t0 = kc * tpc
-                nt = min(T, t0 + tpc) - t0
-                for t in range(nt + 3):
-                    tt = t0 + (t if t < nt else 0)
-                    first, last = tt * KT, min(tt * KT + KT - 1, L - 1)
-                    k.check(kblk + first * kstr, kblk + last * kstr + D * 2, f"{w.name} row statistics h{h} g{g}")
-                    n += 1
-    q0 = (la + V * L) * Hq * D * 2
-    for g in range(Hkv):
-        for c in range(cdiv(R, CS_ROWS) + 2):
-            for row in range(CS_ROWS):
-                r = c * CS_ROWS + row
-                tok, head = (r % nq, g * G + r // nq) if r < R else (0, g * G)
-                off = q0 + (tok * Hq + head) * D * 2
-                q.check(off, off + D * 2, f"{w.name} column sums g{g} chunk {c}")
-            n += 1
+                nts = [min(T, t0 + tpc) - t0]
+                if ctx:
+                    nts = []
+                    for rt in range(cdiv(R, RS_ROWS)):
+                        r_lo, r_hi = rt * RS_ROWS, min(R, rt * RS_ROWS + RS_ROWS) - 1
+                        last = ntok - 1 if r_lo // ntok != r_hi // ntok else r_hi % ntok
+                        nts.append(max(0, min(min(T, t0 + tpc) - t0, cdiv(last + 1, KT) - t0)))
+                for nt in sorted(set(nts)):
+                    for t in range(nt + 3):
+                        tt = t0 + (t if t < nt else 0)
+                        first, last = tt * KT, min(tt * KT + KT - 1, L - 1)
+                        k.check(kblk + first * kstr, kblk + last * kstr + D * 2,
+                                f"{w.name} row statistics h{h} g{g}")
+                        n += 1
+    for h in range(V if ctx else 1):
+        q0 = ((la + h * L) if ctx else (la + V * L)) * Hq * D * 2
+        q_end = q0 + ntok * Hq * D * 2     # the column sums' Q range ends here
+        for g in range(Hkv):
+            for c in range(cdiv(R, CS_ROWS) + 2):
+                for row in range(CS_ROWS):
+                    r = c * CS_ROWS + row
+                    tok, head = (r % ntok, g * G + r // ntok) if r < R else (0, g * G)
+                    off = q0 + (tok * Hq + head) * D * 2
+                    q.check(off, off + D * 2, f"{w.name} column sums h{h} g{g} chunk {c}")
+                    assert off + D * 2 <= q_end, f"{w.name}: column-sum copy past its range"
+                n += 1
     return n
 
 
@@ -203,6 +221,12 @@ FULL = [W.QWEN3B_32K, W.QWEN7B_64K, W.QWEN3B_128K, W.QWEN3B_128K.with_(lp=8064),
 @pytest.mark.parametrize("w", SMALL + FULL, ids=lambda w: f"{w.name}_lp{w.lp}")
 def test_score_copies_in_bounds(w):
     assert score_copies(w, w.head_dim) > 0 or w.n_query == 0
+
+
+@pytest.mark.parametrize("w", SMALL + [W.QWEN3B_32K, W.QWEN3B_32K_PAGE_DEFAULTS_Q128, W.LLAMA8B_128K_TEXT],
+                         ids=lambda w: w.name)
+def test_context_score_copies_in_bounds(w):
+    assert score_copies(w, w.head_dim, ctx=True) > 0
 
 
 @pytest.mark.parametrize("w", SMALL + FULL, ids=lambda w: f"{w.name}_lp{w.lp}")
