@@ -130,7 +130,11 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k,
 /*
  * Workspace bytes spava_score_topk_context needs: as spava_score_topk_ws_bytes
  * with the block's L tokens as the scoring rows, float32 [V][Hkv][L*G] for
- * float32 plans and float32 [C][V][Hkv][L*G][2] for bf16 plans.
+ * float32 plans and float32 [V][Hkv][L*G][2] (one key chunk) for bf16 plans;
+ * bf16 plans
+ * add (from the next 256-byte boundary) float32 [Z][V][Hkv][L] column sums of
+ * Z = G * ceil(L / S) row splits, S = max(1024, 32 * ceil(ceil(L/8) / 32))
+ * tokens each, when Z > 1.
  */
 size_t spava_score_topk_context_ws_bytes(const spava_plan* plan);
 

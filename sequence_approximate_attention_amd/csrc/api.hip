@@ -79,12 +79,15 @@ AttnArgs make_args(const spava_plan* p) {
 // query selector's rows are the query block's tokens, the context selector's
 // the block's own tokens (each times the G heads of a group).
 size_t stats_bytes(const spava_plan* p, bool ctx) {
-  const size_t ntok = ctx ? (size_t)p->host_len : (size_t)p->n_query;
-  const size_t R = ntok * (p->n_q_heads / p->n_kv_heads);
-  const size_t rows = (size_t)p->n_hosts * p->n_kv_heads * R;
-  const size_t bytes = p->dtype == SPAVA_F32
-                           ? rows * sizeof(float)
-                           : rows * (size_t)score_bf16_key_chunks(p->host_len) * sizeof(float2);
+  size_t bytes;
+  if (p->dtype == SPAVA_F32) {
+    const size_t ntok = ctx ? (size_t)p->host_len : (size_t)p->n_query;
+    bytes = (size_t)p->n_hosts * p->n_kv_heads * ntok * (p->n_q_heads / p->n_kv_heads) * sizeof(float);
+  } else {
+    AttnArgs a = make_args(p);
+    a.score_ctx = ctx ? 1 : 0;
+    bytes = score_bf16_ws_bytes(a);
+  }
   return (bytes + 255) / 256 * 256;
 }
 
@@ -122,7 +125,7 @@ int score_topk(const char* name, bool ctx, const spava_plan* plan, const void* q
     }
     e = launch_colsum_f32(a, scores, s);
   } else {
-    e = launch_score_bf16(a, (float2*)ws, scores, s);
+    e = launch_score_bf16(a, ws, scores, s);
   }
   if (e != hipSuccess) return launched(e, "block scores");
   e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);

@@ -22,12 +22,16 @@
 // are skipped.
 //
 //   colsum_kernel: combines each row's chunk partials into its log2-domain
-//     log-sum-exp, then for 256 keys per workgroup sums exp2(s - lse) over all
-//     rows.  Each wave keeps 64 keys' fragments in registers; the two halves
-//     of the workgroup (4 waves each) take alternate 32-row chunks, whose Q
-//     tiles are copied into a 3-slot LDS ring per half, two chunks ahead.
-//     Column sums accumulate per chunk in float32, across chunks in float64,
-//     in a fixed order (deterministic).
+//     log-sum-exp, then for 256 keys per workgroup sums exp2(s - lse) over the
+//     rows of its row split.  Each wave keeps 64 keys' fragments in registers;
+//     the two halves of the workgroup (4 waves each) take alternate 32-row
+//     chunks, whose Q tiles are copied into a 3-slot LDS ring per half, two
+//     chunks ahead.  Column sums accumulate per chunk in float32, across
+//     chunks in float64, in a fixed order (deterministic).  The query rows
+//     form one split (the sums go straight to the scores); the context
+//     selector splits each head's tokens into ranges of at least 1024, each
+//     workgroup starting at its first key's token, and colsum_reduce_kernel
+//     adds the splits' float partials in split order.
 #include "lds_dma.h"
 
 namespace spava {
@@ -111,7 +115,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
   const int n_units = VH * KC * RT;
   const int b = xcd_unit(blockIdx.x, RT);
   if (b >= n_units) return;
-  const int rt = b % RT;
+  // Context selector: row tiles of later tokens see more keys; they start first.
+  const int rt = CTX ? RT - 1 - b % RT : b % RT;
   const int kc = (b / RT) % KC;
   const int hg = b / (RT * KC);
   const int h = hg / a.Hkv;
@@ -121,21 +126,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
 
   // This lane's two scoring rows (one per 32-column block).
   int r[2];
-  bf16x8 qf[2][NC];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    r[qb] = rt * kRsBM + wave * kRsWaveRows + 32 * qb + col;
-    const bool valid = r[qb] < R;
-    const uint16_t* qp = (const uint16_t*)a.q + q_row_elem(a, sr, g, valid ? r[qb] : 0) + 8 * hi;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qf[qb][c] = *(const bf16x8*)(qp + 16 * c);
-      if (!valid) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][c][e] = (__bf16)0.0f;
-      }
-    }
-  }
+  for (int qb = 0; qb < 2; ++qb) r[qb] = rt * kRsBM + wave * kRsWaveRows + 32 * qb + col;
 
   // The chunk's tiles [t0, t0 + nt) of block h; keys past the block's end
   // are masked.
@@ -150,7 +142,29 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
     nt = max(0, min(nt, ceil_div(last_token(r_lo, r_hi, sr.ntok) + 1, kBN) - t0));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) lim_row[qb] = (r[qb] < R) ? r[qb] % sr.ntok + 1 : 0;
+    if (nt == 0) {   // the whole chunk lies above the diagonal: an empty partial
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        if (hi == 0 && r[qb] < R) part[((long)kc * VH + hg) * R + r[qb]] = make_float2(-INFINITY, 0.0f);
+      return;
+    }
   }
+
+  bf16x8 qf[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const bool valid = r[qb] < R;
+    const uint16_t* qp = (const uint16_t*)a.q + q_row_elem(a, sr, g, valid ? r[qb] : 0) + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[qb][c] = *(const bf16x8*)(qp + 16 * c);
+      if (!valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qb][c][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
   const int kstride2 = a.Hkv * D * 2;
   const uint16_t* kblk = (const uint16_t*)a.k + ((long)(a.la + h * a.L) * a.Hkv + g) * D;
   const u32x4 rs_blk = make_rsrc(kblk, (unsigned)a.L * (unsigned)kstride2);
@@ -238,7 +252,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
 constexpr int kCsHalves = 2;
 constexpr int kCsWavesPerHalf = 4;
 constexpr int kCsThreads = kCsHalves * kCsWavesPerHalf * 64;
-constexpr int kCsKeys = kCsWavesPerHalf * 64;    // keys per workgroup
+constexpr int kCsKbQuery = 2;                    // 32-key blocks per wave: query rows
+constexpr int kCsKbCtx = 3;                      // ... context selector
 constexpr int kCsRows = 32;                      // rows per chunk
 constexpr int kCsSlots = 3;                      // Q tile ring per half
 constexpr int kCsLseRows = 4096;                 // rows of the LSE table per pass
@@ -271,9 +286,15 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
     const int blk = w4 * G::QINST + j;
     const int row = blk * G::RPI + q;   // row within the chunk
     int tok = i0 + row, head = a0;
-    while (tok >= ntok) {               // at most 32 / ntok + 1 steps
-      tok -= ntok;
-      ++head;
+    if (ntok >= kCsRows) {              // at most one step to the next head
+      const bool wrap = tok >= ntok;
+      tok -= wrap ? ntok : 0;
+      head += wrap ? 1 : 0;
+    } else {
+      while (tok >= ntok) {             // at most 32 / ntok + 1 steps
+        tok -= ntok;
+        ++head;
+      }
     }
     if (r0 + row >= R) {
       tok = 0;
@@ -285,16 +306,19 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
   }
 }
 
-template <int D, bool CTX>
+template <int D, bool CTX, int KB>
 __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int KC,
                                                                const float2* __restrict__ part,
-                                                               float* __restrict__ scores) {
+                                                               float* __restrict__ scores,
+                                                               float* __restrict__ cpart, int splits_per_head,
+                                                               int split_rows) {
   using G = CsGeo<D>;
   constexpr int NC = G::NC;
   constexpr int QRB = G::QRB;
   __shared__ __attribute__((aligned(1024))) char sQ[kCsHalves * kCsSlots * G::QBYTES];
   __shared__ __attribute__((aligned(16))) float sLse[kCsLseRows];
-  __shared__ double sAcc[kCsWavesPerHalf * 2 * 64];
+  __shared__ double sAcc[kCsWavesPerHalf * KB * 64];
+  constexpr int kKeys = kCsWavesPerHalf * 32 * KB;   // keys per workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -310,13 +334,27 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   const int R = sr.R;
   const int VH = a.V * a.Hkv;
   const long kstr = (long)a.Hkv * D;
-  const int key0 = blockIdx.x * kCsKeys + w4 * 64;
+  const int kw0 = blockIdx.x * kKeys;   // the workgroup's first key
+  const int key0 = kw0 + w4 * 32 * KB;
+  // Rows [r_begin, r_end) of this workgroup's split.  Context selector: a
+  // range of one head's tokens, starting no earlier than token kw0 (earlier
+  // tokens see none of the workgroup's keys).
+  int r_begin, r_end;
+  if (CTX) {
+    const int head = blockIdx.z / splits_per_head;
+    const int ts = blockIdx.z % splits_per_head;
+    r_begin = head * sr.ntok + max(ts * split_rows, kw0);
+    r_end = head * sr.ntok + min(sr.ntok, (ts + 1) * split_rows);
+  } else {
+    r_begin = blockIdx.z * split_rows;
+    r_end = min(R, r_begin + split_rows);
+  }
   const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
 
-  // This wave's 64 keys as B-operand fragments (K^T: 16 channels x 32 keys).
-  bf16x8 kf[2][NC];
+  // This wave's 32 * KB keys as B-operand fragments (K^T: 16 channels x 32 keys).
+  bf16x8 kf[KB][NC];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int j = min(key0 + 32 * kb + col, a.L - 1);
     const uint16_t* kr = kbase + (long)j * kstr + 8 * hi;
 #pragma unroll
@@ -328,10 +366,12 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
                                (unsigned)sr.ntok * (unsigned)a.Hq * (unsigned)D * 2u);
   char* const myq = sQ + half * kCsSlots * G::QBYTES;
   const float sl2 = a.scale_log2;
-  double acc[2] = {0.0, 0.0};
+  double acc[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) acc[kb] = 0.0;
 
-  for (int rb = 0; rb < R; rb += kCsLseRows) {
-    const int nrows = min(kCsLseRows, R - rb);
+  for (int rb = r_begin; rb < r_end; rb += kCsLseRows) {
+    const int nrows = min(kCsLseRows, r_end - rb);
     const int nch = ceil_div(nrows, kCsRows);
     const int nj = ceil_div(nch, kCsHalves);   // chunks per half (the last may be empty)
     __syncthreads();                           // previous pass done with sLse
@@ -342,12 +382,12 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
       cs_issue<D>(a, rs_q, sr.ntok, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
     }
     // ... while the row LSEs are combined from the chunk partials:
-    // lse = M + log2(sum_k l_k 2^(m_k - M)); rows past R get +inf (weight 0).
+    // lse = M + log2(sum_k l_k 2^(m_k - M)); rows past r_end get +inf (weight 0).
     // All of a row's partials are loaded at once (KC <= kMaxKeyChunks).
     for (int i = tid; i < nch * kCsRows; i += kCsThreads) {
       const int rr = rb + i;
       float lse = INFINITY;
-      if (rr < R) {
+      if (rr < r_end) {
         float2 pk[kMaxKeyChunks];
 #pragma unroll
         for (int k = 0; k < kMaxKeyChunks; ++k)
@@ -374,15 +414,16 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
       }
       const int c = kCsHalves * j + half;
       if (c >= nch) continue;
-      // Context selector: the chunk's tokens t see keys j <= t only.
+      // Context selector: the chunk's tokens t see keys j <= t only.  A
+      // split lies within one head, so the chunk's tokens are t_first + m
+      // (rows at or past r_end have weight 0 whatever the mask says).
       const int r_lo = rb + c * kCsRows;
       int t_first = 0;           // block-local token of the chunk's first row
       bool need_mask = false;
       if (CTX) {
-        const int r_hi = min(R, r_lo + kCsRows) - 1;
-        if (last_token(r_lo, r_hi, sr.ntok) < key0) continue;   // none of this wave's keys is visible
         t_first = r_lo % sr.ntok;
-        need_mask = (r_lo / sr.ntok != r_hi / sr.ntok) || t_first < key0 + 63;
+        if (t_first + kCsRows - 1 < key0) continue;   // none of this wave's keys is visible
+        need_mask = t_first < key0 + 32 * KB - 1;
       }
       const char* qt = myq + (j % kCsSlots) * G::QBYTES;
       // LSE of this lane's accumulator rows m = 8 * (i / 4) + 4 * hi + i % 4.
@@ -390,7 +431,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) lz[gi] = *(const f32x4*)(sLse + c * kCsRows + 8 * gi + 4 * hi);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         f32x16 s;
 #pragma unroll
         for (int c16 = 0; c16 < NC; ++c16) {
@@ -402,8 +443,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
           const int jk = key0 + 32 * kb + col;     // this lane's key
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            int t = t_first + 8 * (i >> 2) + 4 * hi + (i & 3);
-            while (t >= sr.ntok) t -= sr.ntok;     // rows of the next head restart at token 0
+            const int t = t_first + 8 * (i >> 2) + 4 * hi + (i & 3);
             const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lz[i >> 2][i & 3]));
             pz += (jk <= t) ? p : 0.0f;
           }
@@ -420,40 +460,84 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   // Column totals: the lane pair (l, l^32) holds the two row halves of a
   // key's accumulator rows; the second workgroup half's totals are added to
   // the first's in a fixed order.
-  double tot[2];
+  double tot[KB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) tot[kb] = acc[kb] + __shfl_xor(acc[kb], 32);
+  for (int kb = 0; kb < KB; ++kb) tot[kb] = acc[kb] + __shfl_xor(acc[kb], 32);
   __syncthreads();
   if (half == 1) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sAcc[(w4 * 2 + kb) * 64 + lane] = tot[kb];
+    for (int kb = 0; kb < KB; ++kb) sAcc[(w4 * KB + kb) * 64 + lane] = tot[kb];
   }
   __syncthreads();
   if (half == 0 && hi == 0) {
+    float* out = gridDim.z == 1 ? scores + (long)hg * a.L : cpart + ((long)blockIdx.z * VH + hg) * a.L;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int j = key0 + 32 * kb + col;
-      if (j < a.L) scores[(long)hg * a.L + j] = (float)(tot[kb] + sAcc[(w4 * 2 + kb) * 64 + lane]);
+      if (j < a.L) out[j] = (float)(tot[kb] + sAcc[(w4 * KB + kb) * 64 + lane]);
     }
   }
 }
 
-}  // namespace
+// Scores of n = V * Hkv * L keys from the S row splits' partial sums, added
+// in split order.
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ cpart,
+                                                            float* __restrict__ scores, int S, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  double acc = 0.0;
+  for (int z = 0; z < S; ++z) acc += (double)cpart[(long)z * n + i];
+  scores[i] = (float)acc;
+}
 
-// Key chunks per block: 512 keys each, but at most kMaxKeyChunks (longer
-// blocks get proportionally longer chunks).
-int score_bf16_tiles_per_chunk(int L) {
-  const int T = ceil_div(L, kBN);
+// Row splits of the column sums: the query rows form one split; the context
+// selector cuts each head's L tokens into at most 8 ranges of at least 1024
+// tokens (a multiple of the 32-row chunk).
+struct ColSplits {
+  int per_head, rows, total;
+};
+ColSplits col_splits(const AttnArgs& a) {
+  const ScoreRows sr = score_rows(a, 0);
+  ColSplits c;
+  if (!a.score_ctx) {
+    c.per_head = 1;
+    c.rows = max(sr.R, 1);
+    c.total = 1;
+  } else {
+    c.rows = max(1024, ceil_div(ceil_div(sr.ntok, 8), kCsRows) * kCsRows);
+    c.per_head = ceil_div(sr.ntok, c.rows);
+    c.total = c.per_head * a.G;
+  }
+  return c;
+}
+
+// Key tiles per chunk of the row statistics.  Query rows: chunks of 512 keys,
+// but at most kMaxKeyChunks per block (longer blocks get proportionally longer
+// chunks), so that the few query rows still fill the GPU.  Context selector:
+// the block's tokens give enough row tiles; one chunk holds every key, so
+// each row tile's Q is read once.
+int tiles_per_chunk(const AttnArgs& a) {
+  const int T = ceil_div(a.L, kBN);
+  if (a.score_ctx) return T;
   return max(kTilesPerChunk, ceil_div(T, kMaxKeyChunks));
 }
-int score_bf16_key_chunks(int L) { return ceil_div(ceil_div(L, kBN), score_bf16_tiles_per_chunk(L)); }
+int key_chunks(const AttnArgs& a) { return ceil_div(ceil_div(a.L, kBN), tiles_per_chunk(a)); }
+
+size_t part_bytes(const AttnArgs& a) {
+  const size_t bytes = (size_t)key_chunks(a) * a.V * a.Hkv * score_rows(a, 0).R * sizeof(float2);
+  return (bytes + 255) / 256 * 256;
+}
+
+}  // namespace
 
 template <bool CTX>
-hipError_t launch_score_bf16_mode(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
+hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hipStream_t s) {
+  float2* part = (float2*)ws;
+  float* cpart = (float*)((char*)ws + part_bytes(a));
   const int R = score_rows(a, 0).R;
   const int VH = a.V * a.Hkv;
-  const int KC = score_bf16_key_chunks(a.L);
-  const int TPC = score_bf16_tiles_per_chunk(a.L);
+  const int KC = key_chunks(a);
+  const int TPC = tiles_per_chunk(a);
   if (R > 0) {
     const int RT = ceil_div(R, kRsBM);
     const int n = VH * KC * RT;
@@ -465,17 +549,33 @@ hipError_t launch_score_bf16_mode(const AttnArgs& a, float2* part, float* scores
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(ceil_div(a.L, kCsKeys), VH);
+  const ColSplits cs = col_splits(a);
+  constexpr int KB = CTX ? kCsKbCtx : kCsKbQuery;
+  const dim3 grid(ceil_div(a.L, kCsWavesPerHalf * 32 * KB), VH, cs.total);
   if (a.D == 128)
-    hipLaunchKernelGGL((colsum_kernel<128, CTX>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+    hipLaunchKernelGGL((colsum_kernel<128, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+                       cs.per_head, cs.rows);
   else
-    hipLaunchKernelGGL((colsum_kernel<64, CTX>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores);
+    hipLaunchKernelGGL((colsum_kernel<64, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+                       cs.per_head, cs.rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || cs.total == 1) return e;
+  const long n = (long)VH * a.L;
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cpart, scores,
+                     cs.total, n);
   return hipGetLastError();
 }
 
-hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s) {
-  return a.score_ctx ? launch_score_bf16_mode<true>(a, part, scores, s)
-                     : launch_score_bf16_mode<false>(a, part, scores, s);
+hipError_t launch_score_bf16(const AttnArgs& a, void* ws, float* scores, hipStream_t s) {
+  return a.score_ctx ? launch_score_bf16_mode<true>(a, ws, scores, s)
+                     : launch_score_bf16_mode<false>(a, ws, scores, s);
+}
+
+// The (max, sum) partials of every scoring row and key chunk, then (several
+// row splits) the splits' column sums.
+size_t score_bf16_ws_bytes(const AttnArgs& a) {
+  const ColSplits cs = col_splits(a);
+  return part_bytes(a) + (cs.total > 1 ? (size_t)cs.total * a.V * a.Hkv * a.L * sizeof(float) : 0);
 }
 
 }  // namespace spava

@@ -270,10 +270,10 @@ __host__ __device__ inline ScoreRows score_rows(const AttnArgs& a, int h) {
 // ---- launchers (host), defined in the .hip files ----
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
-// bf16 scoring (row statistics over key chunks, then column sums); part holds
-// score_bf16_key_chunks(L) * V * Hkv * nq * G (max, sum) pairs.
-hipError_t launch_score_bf16(const AttnArgs& a, float2* part, float* scores, hipStream_t s);
-int score_bf16_key_chunks(int L);
+// bf16 scoring (row statistics over key chunks, then column sums); ws holds
+// score_bf16_ws_bytes(a) bytes.
+hipError_t launch_score_bf16(const AttnArgs& a, void* ws, float* scores, hipStream_t s);
+size_t score_bf16_ws_bytes(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s);
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);

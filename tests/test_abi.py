@@ -68,9 +68,15 @@ def test_workspace_sizes():
     # float32 scoring: one log-sum-exp float per (block, KV head, query row), 256-byte rounded
     assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 16 * 2 * 4
     assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=3)) == 256
-    # context selector: the block's L tokens (times G heads) are the scoring rows
-    assert S.spava_score_topk_context_ws_bytes(p) == 1 * 4 * 1 * 128 * 2 * 8
-    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16)) == 2 * 4 * 1 * 1000 * 2 * 8
+    # context selector: the block's L tokens (times G heads) are the scoring
+    # rows, one key chunk; bf16 adds float column sums of each head's row
+    # split(s) of >= 1024 tokens
+    assert S.spava_score_topk_context_ws_bytes(p) == 1 * 4 * 1 * 128 * 2 * 8 + 2 * 4 * 1 * 128 * 4
+    assert (S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16))
+            == 1 * 4 * 1 * 1000 * 2 * 8 + 2 * 4 * 1 * 1000 * 4)
+    # L = 3000: 3 splits of 1024 tokens per head
+    assert (S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=3000, lp=16))
+            == 1 * 4 * 1 * 3000 * 2 * 8 + 3 * 2 * 4 * 1 * 3000 * 4)
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4
     assert S.spava_score_topk_context_ws_bytes(plan(lp=999)) == 0

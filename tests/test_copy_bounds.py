@@ -9,6 +9,7 @@ only: no GPU is used.  A tensor whose size is a multiple of the allocator's
 2 MiB granule has no slack behind it, so a read past its end can fault; this
 is the check that would have caught such reads.
 """
+import numpy as np
 import pytest
 
 import workloads as W
@@ -169,7 +170,7 @@ def score_copies(w, D, ctx=False):
     if R == 0:
         return 0
     T = cdiv(L, KT)
-    tpc = max(8, cdiv(T, 16))
+    tpc = T if ctx else max(8, cdiv(T, 16))   # the context selector takes all keys in one chunk
     kc_n = cdiv(T, tpc)
     kstr = Hkv * D * 2
     n = 0
@@ -192,18 +193,21 @@ def score_copies(w, D, ctx=False):
                         k.check(kblk + first * kstr, kblk + last * kstr + D * 2,
                                 f"{w.name} row statistics h{h} g{g}")
                         n += 1
+    # Column sums: a chunk copy starts at any row r0 < R of a split (or at R
+    # for the look-ahead past a split's last chunk) and covers rows r0..r0+31;
+    # row r < R is token r % ntok of head g*G + r // ntok, rows >= R read row 0.
+    r = np.arange(R + CS_ROWS)
+    tok = np.where(r < R, r % ntok, 0)
+    head = np.where(r < R, r // ntok, 0)
     for h in range(V if ctx else 1):
         q0 = ((la + h * L) if ctx else (la + V * L)) * Hq * D * 2
         q_end = q0 + ntok * Hq * D * 2     # the column sums' Q range ends here
         for g in range(Hkv):
-            for c in range(cdiv(R, CS_ROWS) + 2):
-                for row in range(CS_ROWS):
-                    r = c * CS_ROWS + row
-                    tok, head = (r % ntok, g * G + r // ntok) if r < R else (0, g * G)
-                    off = q0 + (tok * Hq + head) * D * 2
-                    q.check(off, off + D * 2, f"{w.name} column sums h{h} g{g} chunk {c}")
-                    assert off + D * 2 <= q_end, f"{w.name}: column-sum copy past its range"
-                n += 1
+            off = q0 + ((tok * Hq + g * G + head) * D) * 2
+            lo, hi = int(off.min()), int(off.max()) + D * 2
+            q.check(lo, hi, f"{w.name} column sums h{h} g{g}")
+            assert hi <= q_end, f"{w.name}: column-sum copy past its range"
+            n += len(r)
     return n
 
 
