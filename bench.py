@@ -2,7 +2,10 @@
 """Throughput of one approximate-attention prefill layer on one MI355X.
 
 A step is one pass of the whole path on inputs already resident in HBM:
-spava_score_topk -> spava_gather_passing -> spava_attn_fwd -> spava_lse_merge.
+spava_score_topk -> spava_gather_passing -> spava_attn_fwd -> spava_lse_merge
+(--order partials-first: the attention's LOCAL phase, scores from the query
+partials, gather, the PASSING phase, merge; --selector context: the
+context-driven selector in place of spava_score_topk).
 Workload: Qwen2.5-VL-3B-like attention at 32K tokens (16 query / 2 KV heads,
 d=128; anchor 2048; 8 virtual hosts x 3840; query 128; lp=1024), bf16.
 
@@ -133,6 +136,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    ap.add_argument("--order", choices=("one-pass", "partials-first"), default="one-pass",
+                    help="one-pass: score, gather, one attention call; partials-first: the rows "
+                         "that need no passing block first, scores from the query partials' LSEs, "
+                         "then gather and the remaining rows (Figure 5 ordering)")
     ap.add_argument("--selector", choices=("query", "context"), default="query",
                     help="which rule scores the keys: the query block's attention (the pages' "
                          "method) or each block's own tokens (the referee's alternative)")
@@ -165,19 +172,31 @@ def main():
     stream = torch.cuda.current_stream()
     q0 = wl.n_anchor + wl.n_hosts * wl.host_len
 
+    if args.order == "partials-first" and args.selector == "context":
+        print("--order partials-first scores from the query partials; it takes the query selector",
+              file=sys.stderr)
+        sys.exit(2)
+    attn = lambda phase: S.spava_attn_fwd_phase(plan, phase, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse,
+                                                bufs.o_part, bufs.lse_part, bufs.ws_attn, stream)
+    rec = lambda ev, i: ev[i].record(stream) if ev is not None else None
+
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        score_topk(plan, q, k, bufs.scores, bufs.idx, ws_score, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        # events: 0 | score | 1 | gather | 2 | attention | 3 | merge | 4; in the
+        # partials-first order the attention is split around score + gather
+        # (local phase between 5 and 0, passing phase between 2 and 3).
+        if args.order == "partials-first":
+            rec(ev, 5)
+            attn(S.SPAVA_PHASE_LOCAL)
+            rec(ev, 0)
+            S.spava_score_topk_from_partials(plan, q, k, bufs.lse_part, bufs.scores, bufs.idx, stream)
+        else:
+            rec(ev, 0)
+            score_topk(plan, q, k, bufs.scores, bufs.idx, ws_score, stream)
+        rec(ev, 1)
         S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        S.spava_attn_fwd(plan, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse, bufs.o_part,
-                         bufs.lse_part, bufs.ws_attn, stream)
-        if ev is not None:
-            ev[3].record(stream)
+        rec(ev, 2)
+        attn(S.SPAVA_PHASE_PASSING if args.order == "partials-first" else S.SPAVA_PHASE_ALL)
+        rec(ev, 3)
         S.spava_lse_merge(bufs.o_part, bufs.lse_part, bufs.o[q0:], plan.n_q_heads * plan.head_dim,
                           bufs.lse[:, q0:], plan.n_tokens, stream)
         if ev is not None:
@@ -193,7 +212,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -206,7 +225,10 @@ def main():
     for ev in events:
         stage["score_topk"].append(ev[0].elapsed_time(ev[1]))
         stage["gather"].append(ev[1].elapsed_time(ev[2]))
-        stage["attn_fwd"].append(ev[2].elapsed_time(ev[3]))
+        attn_ms_i = ev[2].elapsed_time(ev[3])
+        if args.order == "partials-first":
+            attn_ms_i += ev[5].elapsed_time(ev[0])
+        stage["attn_fwd"].append(attn_ms_i)
         stage["lse_merge"].append(ev[3].elapsed_time(ev[4]))
     stage_ms = {kk: float(np.mean(vv)) for kk, vv in stage.items()}
     attn_ms = stage_ms["attn_fwd"]
@@ -230,7 +252,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.n_tokens, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "anchor": wl.n_anchor,
                    "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp,
-                   "selector": args.selector},
+                   "selector": args.selector, "order": args.order},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(wl.name)},

@@ -62,6 +62,10 @@ extern "C" {
 #define SPAVA_BF16 0          /* bfloat16 inputs, float32 arithmetic           */
 #define SPAVA_F32 1           /* float32 inputs, float32 arithmetic            */
 
+#define SPAVA_PHASE_ALL 0     /* spava_attn_fwd_phase: every row               */
+#define SPAVA_PHASE_LOCAL 1   /* rows that read no passing block               */
+#define SPAVA_PHASE_PASSING 2 /* context rows of hosts 1..V-1                  */
+
 /*
  * One layer's sequence split (Figure 2 caption) and head geometry.
  *   n_anchor   la  >= 0   anchor tokens (first la rows)
@@ -214,6 +218,44 @@ int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k,
                    const void* v, const void* kp, const void* vp, void* o,
                    float* lse, float* o_part, float* lse_part, void* ws,
                    size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 in two phases, for the ordering of the Spava page's Figure 5 (the
+ * query block's attention over block h comes first and its Q_qr K^(h)T is
+ * reused to score block h).  Arguments, layouts and results as
+ * spava_attn_fwd; the union of the two phases writes exactly what one
+ * spava_attn_fwd call writes, bit for bit.
+ *   SPAVA_PHASE_LOCAL    anchor rows, context rows of host 0 and the query
+ *                        partials o_part/lse_part (no passing block is read:
+ *                        kp, vp may be NULL); fills the V^T copy of ws.
+ *   SPAVA_PHASE_PASSING  context rows of hosts 1..V-1 (o_part, lse_part are
+ *                        not touched and may be NULL); ws must be the
+ *                        workspace the LOCAL phase of the same plan and v
+ *                        filled, unchanged since.
+ *   SPAVA_PHASE_ALL      the same as spava_attn_fwd.
+ * The order of calls is then: spava_attn_fwd_phase(LOCAL) ->
+ * spava_score_topk_from_partials -> spava_gather_passing ->
+ * spava_attn_fwd_phase(PASSING) -> spava_lse_merge.
+ */
+int spava_attn_fwd_phase(const spava_plan* plan, int32_t phase, const void* q,
+                         const void* k, const void* v, const void* kp,
+                         const void* vp, void* o, float* lse, float* o_part,
+                         float* lse_part, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Step 1 after spava_attn_fwd_phase(LOCAL): the same scores and selection as
+ * spava_score_topk, with each query row's softmax normaliser over block h
+ * taken from the query partial over block h (lse_part[h+1], natural log)
+ * instead of a separate pass (Figure 5 caption: Q_qr K^(h)T serves both the
+ * query partial and the scoring).  No workspace.
+ *   lse_part  [V+1][Hq][n_q] float32 as spava_attn_fwd_phase(LOCAL) wrote it
+ *             (may be NULL when n_q == 0)
+ * Other arguments, layouts, alignment and errors as spava_score_topk.
+ */
+int spava_score_topk_from_partials(const spava_plan* plan, const void* q,
+                                   const void* k, const float* lse_part,
+                                   float* scores, int32_t* idx, void* stream);
 
 /*
  * Step 4: log-sum-exp merge of partial attention results (ledger axiom,

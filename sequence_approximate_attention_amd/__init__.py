@@ -23,10 +23,11 @@ LIB_PATH = os.path.join(HERE, "libspava.so")
 
 SPAVA_OK, SPAVA_EINVAL, SPAVA_EUNSUPPORTED, SPAVA_EWORKSPACE, SPAVA_ELAUNCH = range(5)
 SPAVA_BF16, SPAVA_F32 = 0, 1
+SPAVA_PHASE_ALL, SPAVA_PHASE_LOCAL, SPAVA_PHASE_PASSING = 0, 1, 2
 EXPORTS = ("spava_version", "spava_last_error", "spava_plan_check", "spava_score_topk_ws_bytes",
            "spava_score_topk", "spava_gather_passing", "spava_attn_fwd_ws_bytes", "spava_attn_fwd",
            "spava_lse_merge", "spava_score_topk_context_ws_bytes", "spava_score_topk_context",
-           "spava_kv_overlap")
+           "spava_kv_overlap", "spava_attn_fwd_phase", "spava_score_topk_from_partials")
 
 
 class SpavaError(RuntimeError):
@@ -66,6 +67,8 @@ def lib():
         L.spava_score_topk_context_ws_bytes.restype = sz
         L.spava_score_topk_context.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.spava_kv_overlap.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.spava_attn_fwd_phase.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_score_topk_from_partials.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.spava_gather_passing.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.spava_attn_fwd_ws_bytes.argtypes = [P]
         L.spava_attn_fwd_ws_bytes.restype = sz
@@ -194,6 +197,13 @@ def spava_gather_passing(plan: Plan, k, v, idx, kp, vp, stream=None):
 
 
 def spava_attn_fwd(plan: Plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream=None):
+    spava_attn_fwd_phase(plan, SPAVA_PHASE_ALL, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream)
+
+
+def spava_attn_fwd_phase(plan: Plan, phase: int, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream=None):
+    """SPAVA_PHASE_LOCAL: anchor rows, host 0's context rows and the query
+    partials; SPAVA_PHASE_PASSING: context rows of hosts 1..V-1 (after the
+    LOCAL phase, with its workspace); SPAVA_PHASE_ALL: everything."""
     p = plan
     N = p.n_tokens
     _expect(q, (N, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
@@ -205,9 +215,22 @@ def spava_attn_fwd(plan: Plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, st
     _expect(lse, (p.n_q_heads, N), torch.float32, "lse")
     _expect(o_part, (p.n_hosts + 1, p.n_query, p.n_q_heads, p.head_dim), torch.float32, "o_part")
     _expect(lse_part, (p.n_hosts + 1, p.n_q_heads, p.n_query), torch.float32, "lse_part")
-    _check(lib().spava_attn_fwd(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(kp), _ptr(vp),
-                                _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part), _ptr(ws),
-                                ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib().spava_attn_fwd_phase(ctypes.byref(p.c()), phase, _ptr(q), _ptr(k), _ptr(v), _ptr(kp),
+                                      _ptr(vp), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spava_score_topk_from_partials(plan: Plan, q, k, lse_part, scores, idx, stream=None):
+    """Scores and top-lp with the row normalisers taken from the query
+    partials that spava_attn_fwd_phase(LOCAL) wrote."""
+    p = plan
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
+    _expect(lse_part, (p.n_hosts + 1, p.n_q_heads, p.n_query), torch.float32, "lse_part")
+    _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
+    _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
+    _check(lib().spava_score_topk_from_partials(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(lse_part),
+                                                _ptr(scores), _ptr(idx), _stream(stream)))
 
 
 def spava_lse_merge(o_part, lse_part, o, o_row_stride, lse, lse_head_stride, stream=None):
@@ -260,19 +283,34 @@ def alloc_buffers(plan: Plan, device="cuda") -> Buffers:
     )
 
 
-def prefill(plan: Plan, q, k, v, bufs: Buffers | None = None, idx=None, stream=None) -> Buffers:
+def prefill(plan: Plan, q, k, v, bufs: Buffers | None = None, idx=None, stream=None,
+            partials_first: bool = False) -> Buffers:
     """One layer of approximate-attention prefill: score + top-lp (unless
     ``idx`` is given), gather, fused attention, LSE merge.  Returns the
-    buffers; ``bufs.o`` / ``bufs.lse`` hold the layer output."""
+    buffers; ``bufs.o`` / ``bufs.lse`` hold the layer output.
+
+    partials_first: run the rows that need no passing block first (query
+    partials, anchor, host 0) and score from the query partials' LSEs, then
+    gather and run the remaining context rows (Figure 5 ordering); same
+    results."""
     p = plan
     if bufs is None:
         bufs = alloc_buffers(p, q.device)
-    if idx is None:
-        spava_score_topk(p, q, k, bufs.scores, bufs.idx, bufs.ws_score, stream)
-        idx = bufs.idx
-    spava_gather_passing(p, k, v, idx, bufs.kp, bufs.vp, stream)
-    spava_attn_fwd(p, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse, bufs.o_part, bufs.lse_part,
-                   bufs.ws_attn, stream)
+    attn = lambda phase: spava_attn_fwd_phase(p, phase, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse,
+                                              bufs.o_part, bufs.lse_part, bufs.ws_attn, stream)
+    if partials_first:
+        attn(SPAVA_PHASE_LOCAL)
+        if idx is None:
+            spava_score_topk_from_partials(p, q, k, bufs.lse_part, bufs.scores, bufs.idx, stream)
+            idx = bufs.idx
+        spava_gather_passing(p, k, v, idx, bufs.kp, bufs.vp, stream)
+        attn(SPAVA_PHASE_PASSING)
+    else:
+        if idx is None:
+            spava_score_topk(p, q, k, bufs.scores, bufs.idx, bufs.ws_score, stream)
+            idx = bufs.idx
+        spava_gather_passing(p, k, v, idx, bufs.kp, bufs.vp, stream)
+        attn(SPAVA_PHASE_ALL)
     if p.n_query:
         q0 = p.n_anchor + p.n_hosts * p.host_len
         spava_lse_merge(bufs.o_part, bufs.lse_part, bufs.o[q0:], p.n_q_heads * p.head_dim,

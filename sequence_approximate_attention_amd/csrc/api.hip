@@ -71,6 +71,7 @@ AttnArgs make_args(const spava_plan* p) {
   a.n_ctx_units_per_host = ceil_div(a.L, bm) * a.Hq;
   a.n_q_units = ceil_div(a.nq * a.G, bm) * a.Hkv;
   a.n_anchor_units = ceil_div(a.la, bm) * a.Hq;
+  attn_phase_units(a, kPhaseAll, &a.unit_lo, &a.unit_hi);
   return a;
 }
 
@@ -95,6 +96,59 @@ int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SPAVA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
   g_err[0] = 0;
   return SPAVA_OK;
+}
+
+size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
+  const VtLayout vl = VtLayout::make(p->n_anchor, p->n_hosts, p->host_len, p->n_query, p->lp);
+  const size_t main = (size_t)p->n_kv_heads * p->head_dim * vl.main_len * 2;
+  const size_t pass = (size_t)p->n_kv_heads * p->head_dim * vl.pass_len * 2;
+  const size_t main_al = (main + 255) / 256 * 256;
+  if (off_pass) *off_pass = main_al;
+  return main_al + (pass + 255) / 256 * 256;
+}
+
+// Argument checks and launches of the attention, all units or one phase.
+int attn_fwd(const char* name, int phase, const spava_plan* plan, const void* q, const void* k, const void* v,
+             const void* kp, const void* vp, void* o, float* lse, float* o_part, float* lse_part, void* ws,
+             size_t ws_bytes, void* stream) {
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  const bool need_pass = phase != kPhaseLocal && plan->lp > 0 && plan->n_hosts > 1;
+  const bool need_part = phase != kPhasePassing && plan->n_query > 0;
+  if (!q || !k || !v || !o || !lse || !ws || (need_pass && (!kp || !vp)) || (need_part && (!o_part || !lse_part)))
+    return fail(SPAVA_EINVAL, "%s: NULL pointer", name);
+  const void* ptrs[] = {q, k, v, kp, vp, o, lse, o_part, lse_part, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
+  const size_t need = plan->dtype == SPAVA_F32 ? 256 : vt_bytes(plan, nullptr);
+  if (ws_bytes < need) return fail(SPAVA_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a = make_args(plan);
+  attn_phase_units(a, phase, &a.unit_lo, &a.unit_hi);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kp = kp;
+  a.vp = vp;
+  a.o = o;
+  a.lse = lse;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  hipError_t e;
+  if (a.f32) {
+    e = launch_attn_f32(a, s);
+    return launched(e, "attention (float32)");
+  }
+  size_t off_pass = 0;
+  vt_bytes(plan, &off_pass);
+  uint16_t* vt = (uint16_t*)ws;
+  uint16_t* vpt = (uint16_t*)((char*)ws + off_pass);
+  e = launch_vtranspose(a, vt, vpt, phase, s);
+  if (e != hipSuccess) return launched(e, "V transpose");
+  a.vt = vt;
+  a.vpt = vpt;
+  e = launch_attn_bf16(a, s);
+  return launched(e, "attention (bf16)");
 }
 
 // Block scores and top-lp selection with the query rows (ctx = false) or the
@@ -132,14 +186,6 @@ int score_topk(const char* name, bool ctx, const spava_plan* plan, const void* q
   return launched(e, "top-lp selection");
 }
 
-size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
-  const VtLayout vl = VtLayout::make(p->n_anchor, p->n_hosts, p->host_len, p->n_query, p->lp);
-  const size_t main = (size_t)p->n_kv_heads * p->head_dim * vl.main_len * 2;
-  const size_t pass = (size_t)p->n_kv_heads * p->head_dim * vl.pass_len * 2;
-  const size_t main_al = (main + 255) / 256 * 256;
-  if (off_pass) *off_pass = main_al;
-  return main_al + (pass + 255) / 256 * 256;
-}
 
 
 }  // namespace
@@ -222,44 +268,40 @@ size_t spava_attn_fwd_ws_bytes(const spava_plan* plan) {
 int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k, const void* v,
                    const void* kp, const void* vp, void* o, float* lse, float* o_part,
                    float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd("spava_attn_fwd", kPhaseAll, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, ws_bytes,
+                  stream);
+}
+
+int spava_attn_fwd_phase(const spava_plan* plan, int32_t phase, const void* q, const void* k, const void* v,
+                         const void* kp, const void* vp, void* o, float* lse, float* o_part,
+                         float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+  if (phase != SPAVA_PHASE_ALL && phase != SPAVA_PHASE_LOCAL && phase != SPAVA_PHASE_PASSING)
+    return fail(SPAVA_EINVAL, "spava_attn_fwd_phase: phase %d is not SPAVA_PHASE_ALL, _LOCAL or _PASSING", phase);
+  return attn_fwd("spava_attn_fwd_phase", phase, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, ws_bytes,
+                  stream);
+}
+
+int spava_score_topk_from_partials(const spava_plan* plan, const void* q, const void* k, const float* lse_part,
+                                   float* scores, int32_t* idx, void* stream) {
   int rc = check_plan(plan);
   if (rc) return rc;
-  const bool need_pass = plan->lp > 0 && plan->n_hosts > 1;
-  if (!q || !k || !v || !o || !lse || !ws || (need_pass && (!kp || !vp)) ||
-      (plan->n_query > 0 && (!o_part || !lse_part)))
-    return fail(SPAVA_EINVAL, "spava_attn_fwd: NULL pointer");
-  const void* ptrs[] = {q, k, v, kp, vp, o, lse, o_part, lse_part, ws};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(SPAVA_EINVAL, "spava_attn_fwd: pointers must be 16-byte aligned");
-  const size_t need = spava_attn_fwd_ws_bytes(plan);
-  if (ws_bytes < need)
-    return fail(SPAVA_EWORKSPACE, "spava_attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
+  const char* name = "spava_score_topk_from_partials";
+  if (!q || !k || !scores || (plan->lp > 0 && !idx) || (plan->n_query > 0 && !lse_part))
+    return fail(SPAVA_EINVAL, "%s: q, k, scores (idx when lp > 0, lse_part when n_query > 0) must be non-NULL",
+                name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || (idx && !aligned16(idx)) ||
+      (lse_part && !aligned16(lse_part)))
+    return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
   hipStream_t s = (hipStream_t)stream;
   AttnArgs a = make_args(plan);
   a.q = q;
   a.k = k;
-  a.v = v;
-  a.kp = kp;
-  a.vp = vp;
-  a.o = o;
-  a.lse = lse;
-  a.o_part = o_part;
-  a.lse_part = lse_part;
-  hipError_t e;
-  if (a.f32) {
-    e = launch_attn_f32(a, s);
-    return launched(e, "attention (float32)");
-  }
-  size_t off_pass = 0;
-  vt_bytes(plan, &off_pass);
-  uint16_t* vt = (uint16_t*)ws;
-  uint16_t* vpt = (uint16_t*)((char*)ws + off_pass);
-  e = launch_vtranspose(a, vt, vpt, s);
-  if (e != hipSuccess) return launched(e, "V transpose");
-  a.vt = vt;
-  a.vpt = vpt;
-  e = launch_attn_bf16(a, s);
-  return launched(e, "attention (bf16)");
+  a.lse_part = (float*)lse_part;
+  a.score_from_partials = 1;
+  hipError_t e = a.f32 ? launch_colsum_f32(a, scores, s) : launch_score_bf16(a, nullptr, scores, s);
+  if (e != hipSuccess) return launched(e, "block scores");
+  e = launch_topk(scores, idx, a.V * a.Hkv, a.L, a.lp, s);
+  return launched(e, "top-lp selection");
 }
 
 int spava_lse_merge(int32_t n_parts, int32_t n_rows, int32_t n_heads, int32_t head_dim,

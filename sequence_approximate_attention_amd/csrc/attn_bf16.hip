@@ -636,9 +636,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   const int hi = lane >> 5;
   const int col = lane & 31;
 
-  const int n_units = attn_total_units(a);
-  const int b = xcd_unit(blockIdx.x, a.xcd_chunk);
-  if (b >= n_units) return;
+  const int b = a.unit_lo + xcd_unit(blockIdx.x, a.xcd_chunk);
+  if (b >= a.unit_hi) return;
   const Unit u = unit_decode(a, b);
   Runs run;
   unit_runs(a, u, run.r0, run.r1, run.r2);
@@ -844,8 +843,8 @@ int attn_bf16_rows_per_unit() { return kBM; }
 
 hipError_t launch_attn_bf16(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
-  const int n = attn_total_units(a);
-  if (n == 0) return hipSuccess;
+  const int n = a.unit_hi - a.unit_lo;
+  if (n <= 0) return hipSuccess;
   a.xcd_chunk = a.Hq;
   const dim3 grid(xcd_grid(n, a.xcd_chunk));
   if (a.D == 128)

@@ -13,7 +13,7 @@ constexpr int kRows = 128;
 
 template <int D>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a) {
-  const Unit u = unit_decode(a, blockIdx.x);
+  const Unit u = unit_decode(a, a.unit_lo + blockIdx.x);
   Seg segs[3];
   const int nseg = unit_segments(a, u, segs);
   const int r = u.tile * kRows + threadIdx.x;
@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-  const int n = attn_total_units(a);
-  if (n == 0) return hipSuccess;
+  const int n = a.unit_hi - a.unit_lo;
+  if (n <= 0) return hipSuccess;
   if (a.D == 128)
     hipLaunchKernelGGL((attn_f32_kernel<128>), dim3(n), dim3(kRows), 0, s, a);
   else

@@ -45,13 +45,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void vtranspose_kernel(AttnArgs a, uint16_t* __restrict__ vt,
-                                                         uint16_t* __restrict__ vpt) {
+                                                         uint16_t* __restrict__ vpt, int tile0) {
   constexpr int TS = kKeyTile + 2;  // LDS row stride (elements) of the [D][keys] tile
   __shared__ uint16_t sT[D * TS];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int main_tiles = a.vl.main_len / kKeyTile;
-  const int tt = blockIdx.x;
+  const int tt = tile0 + blockIdx.x;
   const bool pass = tt >= main_tiles;
   const int p0 = (pass ? tt - main_tiles : tt) * kKeyTile;
 
@@ -176,13 +176,17 @@ hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void*
   return hipGetLastError();
 }
 
-hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s) {
-  const int tiles = a.vl.main_len / kKeyTile + a.vl.pass_len / kKeyTile;
+hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, int phase, hipStream_t s) {
+  const int main_tiles = a.vl.main_len / kKeyTile;
+  const int pass_tiles = a.vl.pass_len / kKeyTile;
+  const int tile0 = phase == kPhasePassing ? main_tiles : 0;
+  const int tiles = (phase == kPhaseLocal ? 0 : pass_tiles) + (phase == kPhasePassing ? 0 : main_tiles);
+  if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.Hkv);
   if (a.D == 128)
-    hipLaunchKernelGGL((vtranspose_kernel<128>), grid, dim3(256), 0, s, a, vt, vpt);
+    hipLaunchKernelGGL((vtranspose_kernel<128>), grid, dim3(256), 0, s, a, vt, vpt, tile0);
   else
-    hipLaunchKernelGGL((vtranspose_kernel<64>), grid, dim3(256), 0, s, a, vt, vpt);
+    hipLaunchKernelGGL((vtranspose_kernel<64>), grid, dim3(256), 0, s, a, vt, vpt, tile0);
   return hipGetLastError();
 }
 

@@ -73,6 +73,10 @@ __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __re
 #pragma unroll
   for (int c = 0; c < D; ++c) kv[c] = kr[c];
   const float* lse2 = a.stats + (long)hg * R;
+  // Query rows after the attention's first phase: the query partial over
+  // block h holds each row's natural-log LSE over the block's keys.
+  const bool from_part = a.score_from_partials && !a.score_ctx;
+  const float* lse_nat = a.lse_part + (long)(h + 1) * a.Hq * a.nq;
   double acc = 0.0;
   for (int r = 0; r < R; ++r) {
     if (a.score_ctx && r % sr.ntok < j) continue;   // token r % L does not see key j
@@ -82,7 +86,8 @@ __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __re
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < D; ++c) s = fmaf(q[c], kv[c], s);
-    acc += (double)__builtin_amdgcn_exp2f(s * a.scale_log2 - lse2[r]);
+    const float l2 = from_part ? lse_nat[(long)head * a.nq + r % a.nq] * 1.44269504088896340736f : lse2[r];
+    acc += (double)__builtin_amdgcn_exp2f(s * a.scale_log2 - l2);
   }
   scores[gid] = (float)acc;
 }

@@ -382,12 +382,19 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
       cs_issue<D>(a, rs_q, sr.ntok, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
     }
     // ... while the row LSEs are combined from the chunk partials:
-    // lse = M + log2(sum_k l_k 2^(m_k - M)); rows past r_end get +inf (weight 0).
+    // lse = M + log2(sum_k l_k 2^(m_k - M)) (or the query partial's LSE in
+    // log2 units); rows past r_end get +inf (weight 0).
     // All of a row's partials are loaded at once (KC <= kMaxKeyChunks).
     for (int i = tid; i < nch * kCsRows; i += kCsThreads) {
       const int rr = rb + i;
       float lse = INFINITY;
-      if (rr < r_end) {
+      if (!CTX && a.score_from_partials) {
+        // The query partial over block h already holds this row's
+        // natural-log LSE over the block's keys (Figure 5 ordering).
+        if (rr < r_end)
+          lse = a.lse_part[((long)(h + 1) * a.Hq + g * a.G + rr / sr.ntok) * a.nq + rr % sr.ntok] *
+                1.44269504088896340736f;
+      } else if (rr < r_end) {
         float2 pk[kMaxKeyChunks];
 #pragma unroll
         for (int k = 0; k < kMaxKeyChunks; ++k)
@@ -538,7 +545,7 @@ hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hi
   const int VH = a.V * a.Hkv;
   const int KC = key_chunks(a);
   const int TPC = tiles_per_chunk(a);
-  if (R > 0) {
+  if (R > 0 && !(a.score_from_partials && !CTX)) {
     const int RT = ceil_div(R, kRsBM);
     const int n = VH * KC * RT;
     const dim3 grid(xcd_grid(n, RT));

@@ -80,7 +80,9 @@ struct AttnArgs {
   int rows_per_unit;         // BM
   int f32;                   // 1: float32 elements, 0: bf16
   int score_ctx;             // scoring rows: 0 = the query block, 1 = each block's own tokens
+  int score_from_partials;   // 1: row LSEs of the query scoring come from lse_part
   int xcd_chunk;             // units per XCD chunk (see xcd_unit)
+  int unit_lo, unit_hi;      // units [unit_lo, unit_hi) of the launch order run in this launch
 };
 
 struct Unit {
@@ -142,6 +144,18 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
 
 __host__ __device__ inline int attn_total_units(const AttnArgs& a) {
   return a.V * a.n_ctx_units_per_host + a.V * a.n_q_units + a.n_q_units + a.n_anchor_units;
+}
+
+// Phases of the attention (launch order above): the units that read no
+// passing block -- context rows of host 0, the query partials, the anchor --
+// are the tail of the order; the context rows of hosts 1..V-1 are its head.
+// Running the first phase before the selection lets the selection reuse the
+// query partials' row LSEs (Figure 5 ordering).
+enum AttnPhase : int { kPhaseAll = 0, kPhaseLocal = 1, kPhasePassing = 2 };
+__host__ __device__ inline void attn_phase_units(const AttnArgs& a, int phase, int* lo, int* hi) {
+  const int split = (a.V - 1) * a.n_ctx_units_per_host;
+  *lo = phase == kPhaseLocal ? split : 0;
+  *hi = phase == kPhasePassing ? split : attn_total_units(a);
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
@@ -275,7 +289,9 @@ int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
 hipError_t launch_score_bf16(const AttnArgs& a, void* ws, float* scores, hipStream_t s);
 size_t score_bf16_ws_bytes(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
-hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, hipStream_t s);
+// V^T copy of the main rows (phase all / local) and of the passing values
+// (phase all / passing).
+hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, int phase, hipStream_t s);
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);

@@ -123,3 +123,17 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     assert lib.spava_kv_overlap(2, 4, fake, fake, None, None) == S.SPAVA_EINVAL
     assert lib.spava_kv_overlap(2, 4, fake, ctypes.c_void_p(0x10002), fake, None) == S.SPAVA_EINVAL
     assert lib.spava_kv_overlap(0, 4, None, None, None, None) == S.SPAVA_OK
+    # Attention in phases: unknown phase; the LOCAL phase needs no passing
+    # blocks but its partials, the PASSING phase the reverse.
+    assert lib.spava_attn_fwd_phase(ctypes.byref(p), 7, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                    fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert b"phase" in lib.spava_last_error()
+    assert lib.spava_attn_fwd_phase(ctypes.byref(p), S.SPAVA_PHASE_LOCAL, fake, fake, fake, None, None, fake, fake,
+                                    None, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert lib.spava_attn_fwd_phase(ctypes.byref(p), S.SPAVA_PHASE_PASSING, fake, fake, fake, None, fake, fake,
+                                    fake, None, None, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    assert lib.spava_attn_fwd_phase(ctypes.byref(pb), S.SPAVA_PHASE_PASSING, fake, fake, fake, fake, fake, fake,
+                                    fake, None, None, fake, 16, None) == S.SPAVA_EWORKSPACE
+    # Scores from the query partials: lse_part is required when n_query > 0.
+    assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, fake, None, fake, fake, None) == S.SPAVA_EINVAL
+    assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, odd, fake, fake, fake, None) == S.SPAVA_EINVAL

@@ -34,16 +34,16 @@ def heads_to_sample(w):
     return sorted({0, w.n_q_heads - 1} | {g * G for g in range(w.n_kv_heads)})
 
 
-def run_case(w, query_stride=7, dense_check=False, stride=61, heads=None):
+def run_case(w, query_stride=7, dense_check=False, stride=61, heads=None, partials_first=False):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     x, sc = inputs(w)
-    print(f"[fullsize] {w.name} lp={w.lp} N={w.n_tokens}", flush=True)
+    print(f"[fullsize] {w.name} lp={w.lp} N={w.n_tokens} partials_first={partials_first}", flush=True)
     idx_o = O.select_passing(sc, w.lp)
     plan = S.plan_for(w)
     q, k, v = dev_inputs(x, w)
     # 1. Scores and selection, full.
-    bufs = S.prefill(plan, q, k, v)
+    bufs = S.prefill(plan, q, k, v, partials_first=partials_first)
     torch.cuda.synchronize()
     got_sc = np64(bufs.scores)
     rel = np.abs(got_sc - sc) / np.maximum(sc, 1e-30)
@@ -52,7 +52,7 @@ def run_case(w, query_stride=7, dense_check=False, stride=61, heads=None):
     n_diff = check_idx(sc, idx_g, idx_o, w.lp)
     print(f"[fullsize] scores max rel err {rel.max():.2e}; index differences at near-ties: {n_diff}")
     # 2. Gather + attention with the oracle's own selection.
-    bufs2 = S.prefill(plan, q, k, v, idx=torch.from_numpy(idx_o).to(q.device))
+    bufs2 = S.prefill(plan, q, k, v, idx=torch.from_numpy(idx_o).to(q.device), partials_first=partials_first)
     torch.cuda.synchronize()
     kp_o, vp_o = O.gather_passing(x["k"], x["v"], idx_o, w.n_anchor, w.host_len)
     rng = np.random.default_rng(0)
