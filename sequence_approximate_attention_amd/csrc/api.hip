@@ -71,6 +71,15 @@ AttnArgs make_args(const spava_plan* p) {
   a.n_ctx_units_per_host = ceil_div(a.L, bm) * a.Hq;
   a.n_q_units = ceil_div(a.nq * a.G, bm) * a.Hkv;
   a.n_anchor_units = ceil_div(a.la, bm) * a.Hq;
+  // Query-block partials (ceil(L/64) tiles each) go after the hosts whose
+  // shortest context unit (first row tile) walks at least as many tiles.
+  const int t_qblk = ceil_div(a.L, kKeyTile);
+  a.n_ctx_first = 0;
+  for (int h = 0; h < a.V; ++h) {
+    const int t_min = ceil_div(a.la, kKeyTile) + (h > 0 ? ceil_div(h * a.lp, kKeyTile) : 0) +
+                      ceil_div(a.L < bm ? a.L : bm, kKeyTile);
+    if (t_min >= t_qblk) ++a.n_ctx_first;
+  }
   attn_phase_units(a, kPhaseAll, &a.unit_lo, &a.unit_hi);
   return a;
 }
@@ -124,6 +133,7 @@ int attn_fwd(const char* name, int phase, const spava_plan* plan, const void* q,
   if (ws_bytes < need) return fail(SPAVA_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   AttnArgs a = make_args(plan);
+  if (phase != kPhaseAll) a.n_ctx_first = a.V;   // phases split the order after host 1
   attn_phase_units(a, phase, &a.unit_lo, &a.unit_hi);
   a.q = q;
   a.k = k;

@@ -77,6 +77,7 @@ struct AttnArgs {
   int n_ctx_units_per_host;  // ceil(L/BM) * Hq
   int n_q_units;             // ceil(nq*G/BM) * Hkv, per query partial
   int n_anchor_units;        // ceil(la/BM) * Hq
+  int n_ctx_first;           // hosts whose context units precede the query-block partials
   int rows_per_unit;         // BM
   int f32;                   // 1: float32 elements, 0: bf16
   int score_ctx;             // scoring rows: 0 = the query block, 1 = each block's own tokens
@@ -94,9 +95,12 @@ struct Unit {
 };
 
 // Launch order of units (longest rows first, roughly):
-//   context units of host V-1 down to 0 (later row tiles first, heads fastest),
-//   query-block partials of blocks 0..V-1, query partial 0, anchor units.
-// Query-row units are KV-group-major so that units sharing K/V are adjacent.
+//   context units of hosts V-1 down to V-n_ctx_first (later row tiles first,
+//   heads fastest), the query-block partials of blocks 0..V-1, the context
+//   units of the remaining hosts (down to 0), query partial 0, anchor units.
+// n_ctx_first puts the query-block partials (all of length L) after the
+// hosts whose every context unit is at least that long.  Query-row units are
+// KV-group-major so that units sharing K/V are adjacent.
 __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   Unit u;
   u.host = 0;
@@ -106,19 +110,21 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
   const int bm = a.rows_per_unit;
   const int qt = a.n_q_units / a.Hkv;  // query row tiles per KV group
   const int nctx = a.V * a.n_ctx_units_per_host;
-  if (b < nctx) {
+  const int nqb = a.V * a.n_q_units;
+  const int n1 = a.n_ctx_first * a.n_ctx_units_per_host;
+  if (b < n1 || (b >= n1 + nqb && b < nctx + nqb)) {
+    const int c = b < n1 ? b : b - nqb;   // index among the context units
     u.kind = kContext;
-    u.host = a.V - 1 - b / a.n_ctx_units_per_host;
-    int r = b % a.n_ctx_units_per_host;
+    u.host = a.V - 1 - c / a.n_ctx_units_per_host;
+    int r = c % a.n_ctx_units_per_host;
     int ntile = ceil_div(a.L, bm);
     u.head = r % a.Hq;
     u.tile = ntile - 1 - r / a.Hq;
     u.group = u.head / a.G;
     return u;
   }
-  b -= nctx;
-  const int nqb = a.V * a.n_q_units;
-  if (b < nqb) {
+  if (b < n1 + nqb) {
+    b -= n1;
     u.kind = kQueryBlock;
     u.host = b / a.n_q_units;
     int r = b % a.n_q_units;
@@ -126,7 +132,7 @@ __device__ inline Unit unit_decode(const AttnArgs& a, int b) {
     u.tile = r % qt;
     return u;
   }
-  b -= nqb;
+  b -= nctx + nqb;
   if (b < a.n_q_units) {
     u.kind = kQueryHead;
     u.group = b / qt;
@@ -152,6 +158,7 @@ __host__ __device__ inline int attn_total_units(const AttnArgs& a) {
 // Running the first phase before the selection lets the selection reuse the
 // query partials' row LSEs (Figure 5 ordering).
 enum AttnPhase : int { kPhaseAll = 0, kPhaseLocal = 1, kPhasePassing = 2 };
+// The phases need the order with every context host first (n_ctx_first = V).
 __host__ __device__ inline void attn_phase_units(const AttnArgs& a, int phase, int* lo, int* hi) {
   const int split = (a.V - 1) * a.n_ctx_units_per_host;
   *lo = phase == kPhaseLocal ? split : 0;
