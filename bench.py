@@ -58,7 +58,18 @@ def score_flops(w, selector="query") -> float:
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_qwen3b_32k_traffic.md")
-ATTN_SOURCE = os.path.join(ROOT, "sequence_approximate_attention_amd", "csrc", "attn_bf16.hip")
+# The attention kernel's sources: its file and the headers that define its
+# unit order and copy helpers.
+ATTN_SOURCES = [os.path.join(ROOT, "sequence_approximate_attention_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "spava_common.h", "lds_dma.h")]
+
+
+def attn_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
@@ -66,15 +77,13 @@ def measured_traffic(workload):
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was
     taken on another workload or a different kernel source than the one built
     here."""
-    import hashlib
     try:
         fields = {}
         for line in open(TRAFFIC_SUMMARY):
             if " = " in line:
                 key, val = line.strip().split(" = ", 1)
                 fields[key] = val
-        src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if fields.get("kernel_source_sha256") != src or fields.get("workload") != workload:
+        if fields.get("kernel_source_sha256") != attn_source_sha256() or fields.get("workload") != workload:
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -143,6 +152,10 @@ def main():
     ap.add_argument("--selector", choices=("query", "context"), default="query",
                     help="which rule scores the keys: the query block's attention (the pages' "
                          "method) or each block's own tokens (the referee's alternative)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed loop, this many more steps each preceded (untimed) by a "
+                         "512 MiB write that evicts the inputs from L2 and the Infinity Cache; "
+                         "reported as cold_cache, not in value")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -221,6 +234,25 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # Cold-cache steps: the 32K layer's inputs (~0.17 GB) fit in the 256 MB
+    # Infinity Cache, so the loop above runs warm; a real model evicts them
+    # between layers.  Per-step HIP-event time after a 512 MiB write.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 255)
+            step(cold_ev[i])
+        torch.cuda.synchronize()
+        step_ms = [ev[0].elapsed_time(ev[4]) + (ev[5].elapsed_time(ev[0]) if args.order == "partials-first" else 0.0)
+                   for ev in cold_ev]
+        attn_cold = [ev[2].elapsed_time(ev[3]) + (ev[5].elapsed_time(ev[0]) if args.order == "partials-first" else 0.0)
+                     for ev in cold_ev]
+        cold = {"steps": args.cold_steps, "flush_mb": 512, "ms_per_step_median": float(np.median(step_ms)),
+                "attn_ms_median": float(np.median(attn_cold))}
+        del flush
+
     stage = {"score_topk": [], "gather": [], "attn_fwd": [], "lse_merge": []}
     for ev in events:
         stage["score_topk"].append(ev[0].elapsed_time(ev[1]))
@@ -260,6 +292,7 @@ def main():
         "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,
         "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
         "stage_ms": stage_ms,
+        "cold_cache": cold,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.selector)
