@@ -166,9 +166,12 @@ __host__ __device__ inline void attn_phase_units(const AttnArgs& a, int phase, i
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
-// b % 8), and each XCD has its own L2.  Units are therefore dealt to XCDs in
-// chunks of `chunk` consecutive units (units that read the same K/V tiles),
-// keeping the launch order within each XCD.  The grid is padded to a
+// b % 8), and each XCD has its own L2 and dispatches only its own
+// workgroups.  Units are therefore dealt to XCDs in chunks of `chunk`
+// consecutive units (units that read the same K/V tiles), keeping the launch
+// order within each XCD.  Round r of 8 chunks starts at XCD r % 8: with
+// units ordered longest first, a fixed start would give XCD 0 the longest
+// chunk of every round and make it finish last.  The grid is padded to a
 // multiple of 8 * chunk; padding workgroups map past the last unit.
 constexpr int kXcds = 8;
 __host__ __device__ inline int xcd_grid(int n_units, int chunk) {
@@ -177,7 +180,8 @@ __host__ __device__ inline int xcd_grid(int n_units, int chunk) {
 __device__ inline int xcd_unit(int b, int chunk) {
   const int x = b % kXcds;
   const int s = b / kXcds;
-  return ((s / chunk) * kXcds + x) * chunk + s % chunk;
+  const int r = s / chunk;
+  return (r * kXcds + (x + r) % kXcds) * chunk + s % chunk;
 }
 
 // A run of keys that a unit's rows attend to.
