@@ -253,6 +253,8 @@ constexpr int kCsHalves = 2;
 constexpr int kCsWavesPerHalf = 4;
 constexpr int kCsThreads = kCsHalves * kCsWavesPerHalf * 64;
 constexpr int kCsKbQuery = 2;                    // 32-key blocks per wave: query rows
+constexpr int kCsKbQueryWide = 3;                // ... query rows, grids of >= kCsWideGrid workgroups
+constexpr int kCsWideGrid = 1024;
 constexpr int kCsKbCtx = 3;                      // ... context selector
 constexpr int kCsRows = 32;                      // rows per chunk
 constexpr int kCsSlots = 3;                      // Q tile ring per half
@@ -537,6 +539,18 @@ size_t part_bytes(const AttnArgs& a) {
 
 }  // namespace
 
+template <bool CTX, int KB>
+void launch_colsum(const AttnArgs& a, int KC, const float2* part, float* scores, float* cpart, const ColSplits& cs,
+                   hipStream_t s) {
+  const dim3 grid(ceil_div(a.L, kCsWavesPerHalf * 32 * KB), a.V * a.Hkv, cs.total);
+  if (a.D == 128)
+    hipLaunchKernelGGL((colsum_kernel<128, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+                       cs.per_head, cs.rows);
+  else
+    hipLaunchKernelGGL((colsum_kernel<64, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+                       cs.per_head, cs.rows);
+}
+
 template <bool CTX>
 hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hipStream_t s) {
   float2* part = (float2*)ws;
@@ -557,14 +571,14 @@ hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hi
     if (e != hipSuccess) return e;
   }
   const ColSplits cs = col_splits(a);
-  constexpr int KB = CTX ? kCsKbCtx : kCsKbQuery;
-  const dim3 grid(ceil_div(a.L, kCsWavesPerHalf * 32 * KB), VH, cs.total);
-  if (a.D == 128)
-    hipLaunchKernelGGL((colsum_kernel<128, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
-                       cs.per_head, cs.rows);
+  // More keys per wave read each Q fragment into more MFMAs (less LDS
+  // traffic per flop) but give fewer workgroups: the query rows take 96 keys
+  // per wave only when that still leaves a few workgroups per CU.
+  const bool wide = CTX || ceil_div(a.L, kCsWavesPerHalf * 32 * kCsKbQueryWide) * VH * cs.total >= kCsWideGrid;
+  if (wide)
+    launch_colsum<CTX, CTX ? kCsKbCtx : kCsKbQueryWide>(a, KC, part, scores, cpart, cs, s);
   else
-    hipLaunchKernelGGL((colsum_kernel<64, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
-                       cs.per_head, cs.rows);
+    launch_colsum<CTX, kCsKbQuery>(a, KC, part, scores, cpart, cs, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cs.total == 1) return e;
   const long n = (long)VH * a.L;
