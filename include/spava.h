@@ -77,7 +77,18 @@ extern "C" {
  *   lp             passing length, 0 <= lp <= L
  *   dtype          SPAVA_BF16 or SPAVA_F32 (element type of q,k,v,kp,vp,o)
  *   scale          softmax scale; 0 means 1/sqrt(d)
- * N = la + V*L + n_q rows in total; N * max(Hq, Hkv) * d must be < 2^31.
+ *   q_stride_tok, q_stride_head    element strides of q between tokens and
+ *   kv_stride_tok, kv_stride_head  between heads (k and v share theirs);
+ *                  channels are contiguous.  0 means the dense layout
+ *                  (Hq*d, d and Hkv*d, d), so a zero-initialised plan tail
+ *                  keeps the dense tensors below.  Each stride must be a
+ *                  multiple of 16 bytes / element size (rows stay 16-byte
+ *                  aligned); a packed QKV projection output [N][Hq+2Hkv][d]
+ *                  is q = qkv, k = qkv + Hq*d, v = qkv + (Hq+Hkv)*d with
+ *                  token strides (Hq+2Hkv)*d and head strides d.
+ * N = la + V*L + n_q rows in total; N * max(Hq, Hkv) * d must be < 2^31, and
+ * so must the element extent of q and of k/v under their strides.  The
+ * outputs (o, kp, vp, partials) are always dense.
  */
 typedef struct spava_plan {
   int32_t n_anchor;
@@ -90,6 +101,10 @@ typedef struct spava_plan {
   int32_t lp;
   int32_t dtype;
   float scale;
+  int64_t q_stride_tok;
+  int64_t q_stride_head;
+  int64_t kv_stride_tok;
+  int64_t kv_stride_head;
 } spava_plan;
 
 /* SPAVA_VERSION of the built library. */
@@ -120,8 +135,8 @@ size_t spava_score_topk_ws_bytes(const spava_plan* plan);
  * with the softmax over the L keys of block h only.  Selection (ledger axiom:
  * ArgTop_lp): the lp indices first in the order (score descending, index
  * ascending), written in ascending order.
- *   q       [N][Hq][d]      dtype
- *   k       [N][Hkv][d]     dtype
+ *   q       [N][Hq][d]      dtype (plan strides)
+ *   k       [N][Hkv][d]     dtype (plan strides)
  *   scores  [V][Hkv][L]     float32, written (also useful as a diagnostic)
  *   idx     [V][Hkv][lp]    int32 block-local key indices, written
  *   ws      >= spava_score_topk_ws_bytes(plan) bytes of scratch

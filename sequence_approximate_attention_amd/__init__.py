@@ -13,6 +13,7 @@ Layouts (rows = tokens [anchor | V blocks of L | n_q query tokens]):
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from dataclasses import dataclass
 
@@ -41,7 +42,9 @@ class spava_plan(ctypes.Structure):
                 ("host_len", ctypes.c_int32), ("n_query", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("lp", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+                ("kv_stride_tok", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64)]
 
 
 _lib = None
@@ -80,7 +83,8 @@ def lib():
 
 @dataclass(frozen=True)
 class Plan:
-    """One layer's split and head geometry (mirrors ``spava_plan``)."""
+    """One layer's split and head geometry (mirrors ``spava_plan``).  Strides
+    are in elements; 0 means the dense layout."""
     n_anchor: int
     n_hosts: int
     host_len: int
@@ -91,6 +95,10 @@ class Plan:
     lp: int
     dtype: int = SPAVA_BF16
     scale: float = 0.0
+    q_stride_tok: int = 0
+    q_stride_head: int = 0
+    kv_stride_tok: int = 0
+    kv_stride_head: int = 0
 
     @property
     def n_tokens(self) -> int:
@@ -103,7 +111,24 @@ class Plan:
     def c(self) -> spava_plan:
         return spava_plan(self.n_anchor, self.n_hosts, self.host_len, self.n_query,
                           self.n_q_heads, self.n_kv_heads, self.head_dim, self.lp,
-                          self.dtype, float(self.scale))
+                          self.dtype, float(self.scale), self.q_stride_tok, self.q_stride_head,
+                          self.kv_stride_tok, self.kv_stride_head)
+
+    def q_strides(self):
+        return (self.q_stride_tok or self.n_q_heads * self.head_dim, self.q_stride_head or self.head_dim, 1)
+
+    def kv_strides(self):
+        return (self.kv_stride_tok or self.n_kv_heads * self.head_dim, self.kv_stride_head or self.head_dim, 1)
+
+    def with_strides(self, q, k, v) -> "Plan":
+        """The plan with the element strides of the views q [N, Hq, d] and
+        k, v [N, Hkv, d] (k and v must share theirs; channels contiguous)."""
+        if tuple(k.stride()) != tuple(v.stride()):
+            raise ValueError("k and v must have the same strides")
+        if q.stride(2) != 1 or k.stride(2) != 1:
+            raise ValueError("channels must be contiguous")
+        return dataclasses.replace(self, q_stride_tok=q.stride(0), q_stride_head=q.stride(1),
+                                   kv_stride_tok=k.stride(0), kv_stride_head=k.stride(1))
 
 
 def _ptr(t):
@@ -121,7 +146,9 @@ def _check(rc: int):
         raise SpavaError(rc, lib().spava_last_error().decode())
 
 
-def _expect(t, shape, dtype, name):
+def _expect(t, shape, dtype, name, strides=None):
+    """Device tensor of this shape and dtype, contiguous or (q, k, v) with the
+    plan's strides."""
     if t is None:
         return
     if not t.is_cuda:
@@ -130,7 +157,10 @@ def _expect(t, shape, dtype, name):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if not t.is_contiguous():
+    if strides is not None:
+        if t.numel() and tuple(t.stride()) != tuple(strides):
+            raise ValueError(f"{name} has strides {tuple(t.stride())}, the plan says {tuple(strides)}")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
@@ -152,8 +182,8 @@ def spava_attn_fwd_ws_bytes(plan: Plan) -> int:
 
 def spava_score_topk(plan: Plan, q, k, scores, idx, ws, stream=None):
     p = plan
-    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
-    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
     _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
     _check(lib().spava_score_topk(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
@@ -163,8 +193,8 @@ def spava_score_topk(plan: Plan, q, k, scores, idx, ws, stream=None):
 def spava_score_topk_context(plan: Plan, q, k, scores, idx, ws, stream=None):
     """Context-driven selection: the block's own tokens score its keys."""
     p = plan
-    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
-    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
     _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
     _check(lib().spava_score_topk_context(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
@@ -187,8 +217,8 @@ def spava_kv_overlap(idx_a, idx_b, counts, stream=None):
 
 def spava_gather_passing(plan: Plan, k, v, idx, kp, vp, stream=None):
     p = plan
-    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
-    _expect(v, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "v")
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
+    _expect(v, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "v", p.kv_strides())
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
     _expect(kp, (p.n_kv_heads, p.n_hosts, p.lp, p.head_dim), p.torch_dtype, "kp")
     _expect(vp, (p.n_kv_heads, p.n_hosts, p.lp, p.head_dim), p.torch_dtype, "vp")
@@ -206,9 +236,9 @@ def spava_attn_fwd_phase(plan: Plan, phase: int, q, k, v, kp, vp, o, lse, o_part
     LOCAL phase, with its workspace); SPAVA_PHASE_ALL: everything."""
     p = plan
     N = p.n_tokens
-    _expect(q, (N, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
-    _expect(k, (N, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
-    _expect(v, (N, p.n_kv_heads, p.head_dim), p.torch_dtype, "v")
+    _expect(q, (N, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
+    _expect(k, (N, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
+    _expect(v, (N, p.n_kv_heads, p.head_dim), p.torch_dtype, "v", p.kv_strides())
     _expect(kp, (p.n_kv_heads, p.n_hosts, p.lp, p.head_dim), p.torch_dtype, "kp")
     _expect(vp, (p.n_kv_heads, p.n_hosts, p.lp, p.head_dim), p.torch_dtype, "vp")
     _expect(o, (N, p.n_q_heads, p.head_dim), p.torch_dtype, "o")
@@ -224,8 +254,8 @@ def spava_score_topk_from_partials(plan: Plan, q, k, lse_part, scores, idx, stre
     """Scores and top-lp with the row normalisers taken from the query
     partials that spava_attn_fwd_phase(LOCAL) wrote."""
     p = plan
-    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q")
-    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k")
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
     _expect(lse_part, (p.n_hosts + 1, p.n_q_heads, p.n_query), torch.float32, "lse_part")
     _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")

@@ -42,6 +42,25 @@ int check_plan(const spava_plan* p) {
   const double H = p->n_q_heads > p->n_kv_heads ? p->n_q_heads : p->n_kv_heads;
   if (N * H * p->head_dim >= 2147483648.0)
     return fail(SPAVA_EINVAL, "N*heads*head_dim must stay below 2^31");
+  // Strides: multiples of 16 bytes, extents below 2^31 elements, and every
+  // run of keys (a block, the anchor, the query block) below 2^31 bytes.
+  const int esz = p->dtype == SPAVA_F32 ? 4 : 2;
+  const int64_t st[4] = {p->q_stride_tok, p->q_stride_head, p->kv_stride_tok, p->kv_stride_head};
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0 || (st[i] * esz) % 16 != 0)
+      return fail(SPAVA_EINVAL, "strides must be >= 0 and multiples of %d elements", 16 / esz);
+  const double q_st = p->q_stride_tok ? (double)p->q_stride_tok : (double)p->n_q_heads * p->head_dim;
+  const double q_sh = p->q_stride_head ? (double)p->q_stride_head : (double)p->head_dim;
+  const double kv_st = p->kv_stride_tok ? (double)p->kv_stride_tok : (double)p->n_kv_heads * p->head_dim;
+  const double kv_sh = p->kv_stride_head ? (double)p->kv_stride_head : (double)p->head_dim;
+  if ((N - 1) * q_st + (p->n_q_heads - 1) * q_sh + p->head_dim >= 2147483648.0 ||
+      (N - 1) * kv_st + (p->n_kv_heads - 1) * kv_sh + p->head_dim >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "q or k/v extends over 2^31 elements under its strides");
+  double run = p->host_len;
+  if (p->n_anchor > run) run = p->n_anchor;
+  if (p->n_query > run) run = p->n_query;
+  if (run * kv_st * esz >= 2147483648.0 || run * q_st * esz >= 2147483648.0)
+    return fail(SPAVA_EINVAL, "a run of keys spans 2^31 bytes or more under the token strides");
   if ((double)p->n_hosts * p->lp * p->n_kv_heads * p->head_dim >= 2147483648.0)
     return fail(SPAVA_EINVAL, "passing blocks too large");
   return SPAVA_OK;
@@ -62,6 +81,10 @@ AttnArgs make_args(const spava_plan* p) {
   a.nq = p->n_query;
   a.lp = p->lp;
   a.N = a.la + a.V * a.L + a.nq;
+  a.q_st = p->q_stride_tok ? p->q_stride_tok : (long)a.Hq * a.D;
+  a.q_sh = p->q_stride_head ? p->q_stride_head : a.D;
+  a.kv_st = p->kv_stride_tok ? p->kv_stride_tok : (long)a.Hkv * a.D;
+  a.kv_sh = p->kv_stride_head ? p->kv_stride_head : a.D;
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)a.D);
   a.scale_log2 = a.scale * 1.44269504088896340736f;
   a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
@@ -264,8 +287,10 @@ int spava_gather_passing(const spava_plan* plan, const void* k, const void* v, c
   if (!aligned16(k) || !aligned16(v) || !aligned16(kp) || !aligned16(vp))
     return fail(SPAVA_EINVAL, "spava_gather_passing: pointers must be 16-byte aligned");
   const int esz = plan->dtype == SPAVA_F32 ? 4 : 2;
+  const AttnArgs a = make_args(plan);
   hipError_t e = launch_gather(k, v, idx, kp, vp, plan->n_anchor, plan->n_hosts, plan->host_len,
-                               plan->n_kv_heads, plan->lp, plan->head_dim * esz, (hipStream_t)stream);
+                               plan->n_kv_heads, plan->lp, plan->head_dim * esz, a.kv_st * esz, a.kv_sh * esz,
+                               (hipStream_t)stream);
   return launched(e, "gather");
 }
 

@@ -105,9 +105,9 @@ __device__ __forceinline__ SegRun empty_run() {
 __device__ __forceinline__ SegRun main_run(const AttnArgs& a, int g, int tok0, int len, int vkey,
                                            int causal) {
   SegRun r;
-  r.k = (const uint16_t*)a.k + ((long)tok0 * a.Hkv + g) * a.D;
+  r.k = (const uint16_t*)a.k + (long)tok0 * a.kv_st + (long)g * a.kv_sh;
   r.vt = a.vt + (long)g * a.D * a.vl.main_len + vkey;
-  r.kstride = a.Hkv * a.D;
+  r.kstride = (int)a.kv_st;
   r.vrow = a.vl.main_len;
   r.len = len;
   r.causal = causal;
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       cx.qtok[qb] = row[qb].tok;
-      const uint16_t* qp = (const uint16_t*)a.q + ((long)row[qb].tok * a.Hq + row[qb].head) * D + 8 * hi;
+      const uint16_t* qp = (const uint16_t*)a.q + (long)row[qb].tok * a.q_st + (long)row[qb].head * a.q_sh + 8 * hi;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         cx.qf[qb][c] = *(const bf16x8*)(qp + 16 * c);

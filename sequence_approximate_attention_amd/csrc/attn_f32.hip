@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a) {
   const int r = u.tile * kRows + threadIdx.x;
   const RowId row = unit_row(a, u, r);
   if (!row.valid) return;
-  const float* qp = (const float*)a.q + ((long)row.tok * a.Hq + row.head) * D;
+  const float* qp = (const float*)a.q + (long)row.tok * a.q_st + (long)row.head * a.q_sh;
   float qv[D], acc[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
                                                      uint8_t* __restrict__ kp,
                                                      uint8_t* __restrict__ vp, int la, int V,
                                                      int L, int Hkv, int lp, int row_bytes,
-                                                     long total_chunks) {
+                                                     long kv_st_bytes, long kv_sh_bytes, long total_chunks) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total_chunks) return;
   const int cpr = row_bytes / 16;
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
   int j = idx[((long)h * Hkv + g) * lp + t];
   j = min(max(j, 0), L - 1);
   const long tok = (long)la + (long)h * L + j;
-  const uint8_t* src = (which ? v : k) + (tok * Hkv + g) * row_bytes + c * 16;
+  const uint8_t* src = (which ? v : k) + tok * kv_st_bytes + g * kv_sh_bytes + c * 16;
   uint8_t* dst = (which ? vp : kp) + ri * row_bytes + c * 16;
   *(uint4*)dst = *(const uint4*)src;
 }
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void vtranspose_kernel(AttnArgs a, uint16_t* _
       tok0 = a.la + a.V * a.L; len = a.nq;
     }
     n_valid = max(0, min(kKeyTile, len - off));
-    src_stride = (long)a.Hkv * D;
-    src_row0 = (long)(tok0 + off) * src_stride + (long)g * D;
+    src_stride = a.kv_st;
+    src_row0 = (long)(tok0 + off) * src_stride + (long)g * a.kv_sh;
   }
 
   constexpr int CPR = D / 8;
@@ -166,13 +166,14 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
 }  // namespace
 
 hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
-                         int la, int V, int L, int Hkv, int lp, int row_bytes, hipStream_t s) {
+                         int la, int V, int L, int Hkv, int lp, int row_bytes, long kv_st_bytes,
+                         long kv_sh_bytes, hipStream_t s) {
   const long total = 2L * Hkv * V * lp * (row_bytes / 16);
   if (total == 0) return hipSuccess;
   const long blocks = (total + 255) / 256;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint8_t*)k,
                      (const uint8_t*)v, idx, (uint8_t*)kp, (uint8_t*)vp, la, V, L, Hkv, lp,
-                     row_bytes, total);
+                     row_bytes, kv_st_bytes, kv_sh_bytes, total);
   return hipGetLastError();
 }
 

@@ -38,12 +38,12 @@ __global__ __launch_bounds__(256) void rowstat_f32_kernel(AttnArgs a) {
   const int tok = sr.tok0 + r % sr.ntok;
   const int head = g * a.G + r / sr.ntok;
   const int nkeys = a.score_ctx ? r % sr.ntok + 1 : a.L;   // keys [0, nkeys) are visible
-  const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
+  const float* q = (const float*)a.q + (long)tok * a.q_st + (long)head * a.q_sh;
   float qv[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) qv[c] = q[c];
-  const long kstr = (long)a.Hkv * D;
-  const float* kb = (const float*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
+  const long kstr = a.kv_st;
+  const float* kb = (const float*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * a.kv_sh;
   float m = -INFINITY, l = 0.0f;
   for (int j = 0; j < nkeys; ++j) {
     const float* kr = kb + (long)j * kstr;
@@ -67,8 +67,7 @@ __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __re
   const int h = hg / a.Hkv, g = hg % a.Hkv;
   const ScoreRows sr = score_rows(a, h);
   const int R = sr.R;
-  const long kstr = (long)a.Hkv * D;
-  const float* kr = (const float*)a.k + (long)(a.la + h * a.L + j) * kstr + (long)g * D;
+  const float* kr = (const float*)a.k + (long)(a.la + h * a.L + j) * a.kv_st + (long)g * a.kv_sh;
   float kv[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) kv[c] = kr[c];
@@ -82,7 +81,7 @@ __global__ __launch_bounds__(256) void colsum_f32_kernel(AttnArgs a, float* __re
     if (a.score_ctx && r % sr.ntok < j) continue;   // token r % L does not see key j
     const int tok = sr.tok0 + r % sr.ntok;
     const int head = g * a.G + r / sr.ntok;
-    const float* q = (const float*)a.q + ((long)tok * a.Hq + head) * D;
+    const float* q = (const float*)a.q + (long)tok * a.q_st + (long)head * a.q_sh;
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < D; ++c) s = fmaf(q[c], kv[c], s);

@@ -63,7 +63,7 @@ struct RsGeo {
 __device__ __forceinline__ long q_row_elem(const AttnArgs& a, const ScoreRows& sr, int g, int r) {
   const int tok = sr.tok0 + r % sr.ntok;
   const int head = g * a.G + r / sr.ntok;
-  return ((long)tok * a.Hq + head) * a.D;
+  return (long)tok * a.q_st + (long)head * a.q_sh;
 }
 
 // Largest block-local token among the rows [r_lo, r_hi] (inclusive) of the
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
     }
   }
 
-  const int kstride2 = a.Hkv * D * 2;
-  const uint16_t* kblk = (const uint16_t*)a.k + ((long)(a.la + h * a.L) * a.Hkv + g) * D;
+  const int kstride2 = (int)a.kv_st * 2;
+  const uint16_t* kblk = (const uint16_t*)a.k + (long)(a.la + h * a.L) * a.kv_st + (long)g * a.kv_sh;
   const u32x4 rs_blk = make_rsrc(kblk, (unsigned)a.L * (unsigned)kstride2);
 
   // The compiler's own wait bookkeeping does not see the LDS copies: settle
@@ -303,7 +303,7 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
       head = 0;
     }
     const int chunk = swz<G::QRB>(row, slot);
-    copy16_to_lds(rs_q, 0u, (unsigned)(((tok * a.Hq + g * a.G + head) * D) * 2 + chunk * 16),
+    copy16_to_lds(rs_q, 0u, (unsigned)(((long)tok * a.q_st + (long)(g * a.G + head) * a.q_sh) * 2 + chunk * 16),
                   (unsigned)(unsigned long long)(qbuf + blk * 1024));
   }
 }
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   const ScoreRows sr = score_rows(a, h);
   const int R = sr.R;
   const int VH = a.V * a.Hkv;
-  const long kstr = (long)a.Hkv * D;
+  const long kstr = a.kv_st;
   const int kw0 = blockIdx.x * kKeys;   // the workgroup's first key
   const int key0 = kw0 + w4 * 32 * KB;
   // Rows [r_begin, r_end) of this workgroup's split.  Context selector: a
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
     r_begin = blockIdx.z * split_rows;
     r_end = min(R, r_begin + split_rows);
   }
-  const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + (long)(a.la + h * a.L) * kstr + (long)g * a.kv_sh;
 
   // This wave's 32 * KB keys as B-operand fragments (K^T: 16 channels x 32 keys).
   bf16x8 kf[KB][NC];
@@ -364,8 +364,9 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   }
   wait_vm<0>();   // as in the row statistics: no compiler wait inside the chunk loop
 
-  const u32x4 rs_q = make_rsrc((const uint16_t*)a.q + (long)sr.tok0 * a.Hq * D,
-                               (unsigned)sr.ntok * (unsigned)a.Hq * (unsigned)D * 2u);
+  // Q rows of the scoring tokens: the range ends at the last one's last head.
+  const u32x4 rs_q = make_rsrc((const uint16_t*)a.q + (long)sr.tok0 * a.q_st,
+                               (unsigned)(((long)(sr.ntok - 1) * a.q_st + (long)(a.Hq - 1) * a.q_sh + D) * 2));
   char* const myq = sQ + half * kCsSlots * G::QBYTES;
   const float sl2 = a.scale_log2;
   double acc[KB];

@@ -70,6 +70,8 @@ struct AttnArgs {
   float* lse_part;
   float* stats;        // float32 scoring: [V][Hkv][nq*G] log2-domain row LSE
   int N, Hq, Hkv, G, D, la, V, L, nq, lp;
+  long q_st, q_sh;     // element strides of q between tokens and between heads
+  long kv_st, kv_sh;   // the same for k and v
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
   VtLayout vl;
@@ -201,17 +203,16 @@ struct Seg {
 // Key segments of a unit (at most 3).  Returns the count.
 __device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
   const int g = u.group;
-  const long kstr = (long)a.Hkv * a.D;
   int n = 0;
   auto main_seg = [&](int tok0, int len, int vt_key_off, int causal) {
     Seg x;
     x.kind = 0;
-    x.k_off = (long)tok0 * kstr + (long)g * a.D;
-    x.k_stride = kstr;
+    x.k_off = (long)tok0 * a.kv_st + (long)g * a.kv_sh;
+    x.k_stride = a.kv_st;
     x.vt_off = (long)g * a.D * a.vl.main_len + vt_key_off;
     x.vt_pass = 0;
     x.v_off = x.k_off;
-    x.v_stride = kstr;
+    x.v_stride = a.kv_st;
     x.len = len;
     x.causal = causal;
     x.tok0 = tok0;
@@ -308,8 +309,10 @@ hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);
 hipError_t launch_overlap(const int32_t* idx_a, const int32_t* idx_b, int32_t* counts, int n_lists,
                           int lp, hipStream_t s);
+// kv_st_bytes, kv_sh_bytes: byte strides of k and v between tokens and heads.
 hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
-                         int la, int V, int L, int Hkv, int lp, int row_bytes, hipStream_t s);
+                         int la, int V, int L, int Hkv, int lp, int row_bytes, long kv_st_bytes,
+                         long kv_sh_bytes, hipStream_t s);
 hipError_t launch_merge(int P, int R, int H, int D, const float* o_part, const float* lse_part,
                         void* o, long o_row_stride, float* lse, long lse_head_stride,
                         int out_bf16, hipStream_t s);

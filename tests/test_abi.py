@@ -27,6 +27,12 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_plan_struct_matches_the_header():
+    # 9 int32 fields and a float, then four int64 strides.
+    assert ctypes.sizeof(S.spava_plan) == 72
+    assert S.spava_plan.q_stride_tok.offset == 40 and S.spava_plan.kv_stride_head.offset == 64
+
+
 def test_version_and_empty_error():
     assert S.lib().spava_version() == 100
     assert isinstance(S.lib().spava_last_error(), bytes)
@@ -53,6 +59,15 @@ def plan(**kw):
     (dict(scale=float("nan")), S.SPAVA_EINVAL),
     (dict(n_hosts=1, host_len=1 << 24, n_q_heads=64, n_kv_heads=8, head_dim=128, lp=0), S.SPAVA_EINVAL),
     (dict(lp=0, n_query=0, n_anchor=0), S.SPAVA_OK),
+    # strides (elements): multiples of 16 bytes, non-negative, bounded extents
+    (dict(q_stride_tok=4 * 64, q_stride_head=64, kv_stride_tok=3 * 64, kv_stride_head=64), S.SPAVA_OK),
+    (dict(q_stride_tok=130), S.SPAVA_EINVAL),
+    (dict(dtype=S.SPAVA_BF16, kv_stride_head=68), S.SPAVA_EINVAL),
+    (dict(dtype=S.SPAVA_BF16, kv_stride_head=72), S.SPAVA_OK),
+    (dict(kv_stride_tok=-64), S.SPAVA_EINVAL),
+    (dict(q_stride_head=1 << 26), S.SPAVA_OK),
+    (dict(q_stride_head=1 << 31), S.SPAVA_EINVAL),
+    (dict(kv_stride_tok=1 << 22), S.SPAVA_EINVAL),
 ])
 def test_plan_check(kw, code):
     assert S.spava_plan_check(plan(**kw)) == code

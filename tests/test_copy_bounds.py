@@ -39,7 +39,23 @@ class Extent:
         assert 0 <= lo and hi <= self.nbytes, f"{what}: {self.name} bytes [{lo}, {hi}) outside [0, {self.nbytes})"
 
 
-def attention_copies(w, D, past_walk="stay"):
+def layout(w, D, strides):
+    """Element strides (q token, q head, kv token, kv head) and the element
+    extents of q and k under them; strides=None is the dense layout,
+    "packed" a QKV projection output [N][Hq+2Hkv][d], "heads_major" [H][N][d]."""
+    N, Hq, Hkv = w.n_tokens, w.n_q_heads, w.n_kv_heads
+    if strides is None:
+        st = (Hq * D, D, Hkv * D, D)
+    elif strides == "packed":
+        st = ((Hq + 2 * Hkv) * D, D, (Hq + 2 * Hkv) * D, D)
+    else:
+        st = (D, N * D, D, N * D)
+    q_ext = (N - 1) * st[0] + (Hq - 1) * st[1] + D
+    k_ext = (N - 1) * st[2] + (Hkv - 1) * st[3] + D
+    return st, q_ext, k_ext
+
+
+def attention_copies(w, D, past_walk="stay", strides=None):
     """Walk the attention kernel's K and V^T cursors of every unit.  With
     past_walk="advance" a cursor keeps stepping over whole tiles after the
     walk (what a cursor whose remaining byte count had gone negative, read as
@@ -48,7 +64,8 @@ def attention_copies(w, D, past_walk="stay"):
     G = Hq // Hkv
     N = la + V * L + nq
     vl = vt_layout(la, V, L, nq, lp)
-    ext = {"k": Extent("k", N * Hkv * D * 2), "kp": Extent("kp", Hkv * V * lp * D * 2),
+    (_, _, kv_st, kv_sh), _, k_ext = layout(w, D, strides)
+    ext = {"k": Extent("k", k_ext * 2), "kp": Extent("kp", Hkv * V * lp * D * 2),
            "vt": Extent("vt", Hkv * D * vl["main_len"] * 2), "vpt": Extent("vpt", Hkv * D * vl["pass_len"] * 2)}
     n_ctx_h = cdiv(L, BM) * Hq
     n_q = cdiv(nq * G, BM) * Hkv
@@ -83,8 +100,8 @@ def attention_copies(w, D, past_walk="stay"):
         gmax = max(toks)
 
         def main(tok0, n, vkey, causal):
-            return dict(kbuf="k", k=(tok0 * Hkv + g) * D * 2, vbuf="vt", vt=(g * D * vl["main_len"] + vkey) * 2,
-                        kstr=Hkv * D * 2, vstr=vl["main_len"] * 2, len=n, causal=causal, tok0=tok0)
+            return dict(kbuf="k", k=(tok0 * kv_st + g * kv_sh) * 2, vbuf="vt", vt=(g * D * vl["main_len"] + vkey) * 2,
+                        kstr=kv_st * 2, vstr=vl["main_len"] * 2, len=n, causal=causal, tok0=tok0)
         runs = [main(0, 0, 0, 0)] * 3
         if kind == "anchor":
             runs = [main(0, la, 0, 1), dict(runs[1], len=0), dict(runs[2], len=0)]
@@ -155,7 +172,7 @@ def attention_copies(w, D, past_walk="stay"):
 RS_ROWS = 256    # rows per row-statistics workgroup
 
 
-def score_copies(w, D, ctx=False):
+def score_copies(w, D, ctx=False, strides=None):
     """Row statistics: K tiles of each key chunk; column sums: Q rows of each
     chunk.  ctx=True walks the context selector: the scoring rows are each
     block's own tokens, and a row-statistics workgroup stops at the tile of
@@ -165,18 +182,19 @@ def score_copies(w, D, ctx=False):
     N = la + V * L + nq
     ntok = L if ctx else nq
     R = ntok * G
-    k = Extent("k", N * Hkv * D * 2)
-    q = Extent("q", N * Hq * D * 2)
+    (q_st, q_sh, kv_st, kv_sh), q_ext, k_ext = layout(w, D, strides)
+    k = Extent("k", k_ext * 2)
+    q = Extent("q", q_ext * 2)
     if R == 0:
         return 0
     T = cdiv(L, KT)
     tpc = T if ctx else max(8, cdiv(T, 16))   # the context selector takes all keys in one chunk
     kc_n = cdiv(T, tpc)
-    kstr = Hkv * D * 2
+    kstr = kv_st * 2
     n = 0
     for h in range(V):
         for g in range(Hkv):
-            kblk = ((la + h * L) * Hkv + g) * D * 2
+            kblk = ((la + h * L) * kv_st + g * kv_sh) * 2
             for kc in range(kc_n):
                 t0 = kc * tpc
                 nts = [min(T, t0 + tpc) - t0]
@@ -200,10 +218,10 @@ def score_copies(w, D, ctx=False):
     tok = np.where(r < R, r % ntok, 0)
     head = np.where(r < R, r // ntok, 0)
     for h in range(V if ctx else 1):
-        q0 = ((la + h * L) if ctx else (la + V * L)) * Hq * D * 2
-        q_end = q0 + ntok * Hq * D * 2     # the column sums' Q range ends here
+        q0 = ((la + h * L) if ctx else (la + V * L)) * q_st * 2
+        q_end = q0 + ((ntok - 1) * q_st + (Hq - 1) * q_sh + D) * 2   # the column sums' Q range ends here
         for g in range(Hkv):
-            off = q0 + ((tok * Hq + g * G + head) * D) * 2
+            off = q0 + (tok * q_st + (g * G + head) * q_sh) * 2
             lo, hi = int(off.min()), int(off.max()) + D * 2
             q.check(lo, hi, f"{w.name} column sums h{h} g{g}")
             assert hi <= q_end, f"{w.name}: column-sum copy past its range"
@@ -236,6 +254,15 @@ def test_context_score_copies_in_bounds(w):
 @pytest.mark.parametrize("w", SMALL + FULL, ids=lambda w: f"{w.name}_lp{w.lp}")
 def test_attention_copies_in_bounds(w):
     assert attention_copies(w, w.head_dim) > 0
+
+
+@pytest.mark.parametrize("strides", ["packed", "heads_major"])
+@pytest.mark.parametrize("w", SMALL[:4] + [W.QWEN3B_32K], ids=lambda w: w.name)
+def test_strided_copies_in_bounds(w, strides):
+    # q, k, v as views of a packed QKV buffer or of head-major tensors.
+    assert attention_copies(w, w.head_dim, strides=strides) > 0
+    assert score_copies(w, w.head_dim, strides=strides) > 0 or w.n_query == 0
+    assert score_copies(w, w.head_dim, ctx=True, strides=strides) > 0
 
 
 @pytest.mark.parametrize("w", [W.QWEN3B_32K_PAGE_DEFAULTS_Q128, W.LLAMA8B_128K_TEXT], ids=lambda w: w.name)

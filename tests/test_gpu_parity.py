@@ -71,8 +71,8 @@ def test_tiny_f32_full_pipeline():
                            w.n_query, w.lp)
     check_idx(ref["scores"], bufs.idx.cpu().numpy(), ref["idx"], w.lp)
     if not np.array_equal(bufs.idx.cpu().numpy(), ref["idx"]):
-        ref = O.approx_prefill(x["q"], x["k"], x["v"], w.n_anchor, w.n_hosts, w.host_len,
-                               w.n_query, w.lp, idx=bufs.idx.cpu().numpy())
+        # A near-tie swap: the attention is compared on the oracle's selection.
+        plan, bufs = run_full(w, x, idx=torch.from_numpy(ref["idx"]).cuda())
     np.testing.assert_array_equal(np64(bufs.kp), ref["kp"])
     np.testing.assert_array_equal(np64(bufs.vp), ref["vp"])
     compare_all(w, x, bufs, ref)
