@@ -145,6 +145,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    ap.add_argument("--lp", type=int, default=None, help="override the workload's passing length")
     ap.add_argument("--order", choices=("one-pass", "partials-first"), default="one-pass",
                     help="one-pass: score, gather, one attention call; partials-first: the rows "
                          "that need no passing block first, scores from the query partials' LSEs, "
@@ -170,6 +171,8 @@ def main():
     import workloads as W
 
     wl = {w.name: w for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS}[args.workload]
+    if args.lp is not None:
+        wl = wl.with_(lp=args.lp)
     x = W.make_inputs(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -287,11 +290,17 @@ def main():
                    "selector": args.selector, "order": args.order},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(wl.name)},
+                     "traffic": measured_traffic(wl.name) if args.lp is None else None},
         "attn_tflop_per_launch": F_attn / 1e12,
         "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,
         "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
         "stage_ms": stage_ms,
+        # HBM-bound stages: algorithmic bytes / HIP-event time.
+        "hbm_gbps": {
+            "gather": 4.0 * wl.n_hosts * wl.n_kv_heads * wl.lp * wl.head_dim * 2 / (stage_ms["gather"] * 1e-3) / 1e9,
+            "lse_merge": ((wl.n_hosts + 1) * wl.n_query * wl.n_q_heads * (wl.head_dim + 1) * 4
+                          + wl.n_query * wl.n_q_heads * (wl.head_dim * 2 + 4)) / (stage_ms["lse_merge"] * 1e-3) / 1e9,
+        },
         "cold_cache": cold,
     }
     if not args.no_cpu_baseline:

@@ -129,14 +129,40 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
   const int c4 = (int)(gid % cq);
   const int a = (int)((gid / cq) % H);
   const int r = (int)(gid / ((long)cq * H));
+  const float* lp_ra = lse_part + (long)a * R + r;                  // + p * H * R
+  const float* op_ra = o_part + ((long)r * H + a) * D + c4 * 4;      // + p * R * H * D
+  const long lp_step = (long)H * R, op_step = (long)R * H * D;
   float m = -INFINITY;
-  for (int p = 0; p < P; ++p) m = fmaxf(m, lse_part[((long)p * H + a) * R + r]);
+#pragma unroll 8
+  for (int p = 0; p < P; ++p) m = fmaxf(m, lp_ra[p * lp_step]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.0f;
   if (m != -INFINITY) {
-    for (int p = 0; p < P; ++p) {
-      const float w = expf(lse_part[((long)p * H + a) * R + r] - m);
-      const float4 x = *(const float4*)(o_part + (((long)p * R + r) * H + a) * D + c4 * 4);
+    // The partials are read kMergeBatch at a time, all loads first, so each
+    // wave keeps that many reads in flight; the sums still run in p order.
+    constexpr int kMergeBatch = 8;
+    int p = 0;
+    for (; p + kMergeBatch <= P; p += kMergeBatch) {
+      float l[kMergeBatch];
+      float4 x[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        l[u] = lp_ra[(p + u) * lp_step];
+        x[u] = *(const float4*)(op_ra + (p + u) * op_step);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = expf(l[u] - m);
+        acc.x += w * x[u].x;
+        acc.y += w * x[u].y;
+        acc.z += w * x[u].z;
+        acc.w += w * x[u].w;
+        wsum += w;
+      }
+    }
+    for (; p < P; ++p) {
+      const float w = expf(lp_ra[p * lp_step] - m);
+      const float4 x = *(const float4*)(op_ra + p * op_step);
       acc.x += w * x.x;
       acc.y += w * x.y;
       acc.z += w * x.z;
