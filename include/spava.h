@@ -122,7 +122,10 @@ int spava_plan_check(const spava_plan* plan);
  * log-sum-exp per row, float32 [V][Hkv][n_q*G]; bf16 plans keep a (max, sum)
  * pair per row and key chunk of the block, float32 [C][V][Hkv][n_q*G][2]
  * with C = ceil(L/512) for L <= 8192 (chunks of 512 keys), else
- * C = ceil(T / ceil(T/16)) with T = ceil(L/64) (at most 16 chunks).
+ * C = ceil(T / ceil(T/16)) with T = ceil(L/64) (at most 16 chunks).  Then,
+ * from the next 256-byte boundary, room for float32 [V][Hkv][L] scores (used
+ * when the caller passes scores = NULL; a caller that passes scores may
+ * provide a workspace without it).
  */
 size_t spava_score_topk_ws_bytes(const spava_plan* plan);
 
@@ -137,7 +140,8 @@ size_t spava_score_topk_ws_bytes(const spava_plan* plan);
  * ascending), written in ascending order.
  *   q       [N][Hq][d]      dtype (plan strides)
  *   k       [N][Hkv][d]     dtype (plan strides)
- *   scores  [V][Hkv][L]     float32, written (also useful as a diagnostic)
+ *   scores  [V][Hkv][L]     float32, written (also useful as a diagnostic);
+ *                           may be NULL: the scores then live in ws
  *   idx     [V][Hkv][lp]    int32 block-local key indices, written
  *   ws      >= spava_score_topk_ws_bytes(plan) bytes of scratch
  * With n_q == 0 every score is 0 and idx = 0..lp-1.

@@ -124,6 +124,12 @@ size_t stats_bytes(const spava_plan* p, bool ctx) {
   return (bytes + 255) / 256 * 256;
 }
 
+// Room for the scores when the caller passes none: float32 [V][Hkv][L] after
+// the statistics.
+size_t scores_bytes(const spava_plan* p) {
+  return ((size_t)p->n_hosts * p->n_kv_heads * p->host_len * sizeof(float) + 255) / 256 * 256;
+}
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SPAVA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
   g_err[0] = 0;
@@ -190,12 +196,14 @@ int score_topk(const char* name, bool ctx, const spava_plan* plan, const void* q
                float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_plan(plan);
   if (rc) return rc;
-  if (!q || !k || !scores || !ws || (plan->lp > 0 && !idx))
-    return fail(SPAVA_EINVAL, "%s: q, k, scores, ws (and idx when lp > 0) must be non-NULL", name);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) || (idx && !aligned16(idx)))
+  if (!q || !k || !ws || (plan->lp > 0 && !idx))
+    return fail(SPAVA_EINVAL, "%s: q, k, ws (and idx when lp > 0) must be non-NULL", name);
+  if (!aligned16(q) || !aligned16(k) || (scores && !aligned16(scores)) || !aligned16(ws) ||
+      (idx && !aligned16(idx)))
     return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
-  const size_t need = stats_bytes(plan, ctx);
+  const size_t need = stats_bytes(plan, ctx) + (scores ? 0 : scores_bytes(plan));
   if (ws_bytes < need) return fail(SPAVA_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
+  if (!scores) scores = (float*)((char*)ws + stats_bytes(plan, ctx));
   if (ctx && (double)plan->host_len * (plan->n_q_heads / plan->n_kv_heads) >= 2147483648.0)
     return fail(SPAVA_EINVAL, "%s: host_len * (n_q_heads / n_kv_heads) must stay below 2^31", name);
   hipStream_t s = (hipStream_t)stream;
@@ -240,7 +248,7 @@ int spava_plan_check(const spava_plan* plan) {
 
 size_t spava_score_topk_ws_bytes(const spava_plan* plan) {
   if (check_plan(plan) != SPAVA_OK) return 0;
-  return stats_bytes(plan, false);
+  return stats_bytes(plan, false) + scores_bytes(plan);
 }
 
 int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float* scores,
@@ -250,7 +258,7 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float
 
 size_t spava_score_topk_context_ws_bytes(const spava_plan* plan) {
   if (check_plan(plan) != SPAVA_OK) return 0;
-  return stats_bytes(plan, true);
+  return stats_bytes(plan, true) + scores_bytes(plan);
 }
 
 int spava_score_topk_context(const spava_plan* plan, const void* q, const void* k, float* scores,

@@ -77,23 +77,26 @@ def test_plan_check(kw, code):
 
 def test_workspace_sizes():
     p = plan(dtype=S.SPAVA_BF16, head_dim=128)
+    r256 = lambda n: (n + 255) // 256 * 256
+    sc = lambda L: r256(4 * 1 * L * 4)       # room for float scores [V][Hkv][L] after the statistics
     # bf16 scoring: a (max, sum) float pair per (key chunk of 512, block, KV head, query row)
-    assert S.spava_score_topk_ws_bytes(p) == 1 * 4 * 1 * 16 * 2 * 8
-    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16)) == 2 * 4 * 1 * 16 * 2 * 8
+    assert S.spava_score_topk_ws_bytes(p) == 1 * 4 * 1 * 16 * 2 * 8 + sc(128)
+    assert (S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16))
+            == 2 * 4 * 1 * 16 * 2 * 8 + sc(1000))
     # float32 scoring: one log-sum-exp float per (block, KV head, query row), 256-byte rounded
-    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 16 * 2 * 4
-    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=3)) == 256
+    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 16 * 2 * 4 + sc(128)
+    assert S.spava_score_topk_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=3)) == 256 + sc(128)
     # context selector: the block's L tokens (times G heads) are the scoring
     # rows, one key chunk; bf16 adds float column sums of each head's row
     # split(s) of >= 1024 tokens
-    assert S.spava_score_topk_context_ws_bytes(p) == 1 * 4 * 1 * 128 * 2 * 8 + 2 * 4 * 1 * 128 * 4
+    assert S.spava_score_topk_context_ws_bytes(p) == 1 * 4 * 1 * 128 * 2 * 8 + 2 * 4 * 1 * 128 * 4 + sc(128)
     assert (S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=1000, lp=16))
-            == 1 * 4 * 1 * 1000 * 2 * 8 + 2 * 4 * 1 * 1000 * 4)
+            == 1 * 4 * 1 * 1000 * 2 * 8 + 2 * 4 * 1 * 1000 * 4 + sc(1000))
     # L = 3000: 3 splits of 1024 tokens per head
     assert (S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_BF16, host_len=3000, lp=16))
-            == 1 * 4 * 1 * 3000 * 2 * 8 + 3 * 2 * 4 * 1 * 3000 * 4)
-    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4
-    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4
+            == 1 * 4 * 1 * 3000 * 2 * 8 + 3 * 2 * 4 * 1 * 3000 * 4 + sc(3000))
+    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4 + sc(128)
+    assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4 + sc(128)
     assert S.spava_score_topk_context_ws_bytes(plan(lp=999)) == 0
     # key-contiguous V: Hkv * d * (pad(la) + V*pad(L) + pad(n_q)) + passing, bf16
     main = 1 * 128 * (64 + 4 * 128 + 64) * 2
@@ -103,6 +106,13 @@ def test_workspace_sizes():
 
 
 def test_null_and_misaligned_pointers_rejected_on_host():
+    # Every call here must fail its host checks: the pointers are fake and
+    # nothing may be launched with them.  Where a GPU is present a check that
+    # let a call through would launch on those addresses, so the test only
+    # runs without one.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer host checks run on machines without a GPU")
     lib = S.lib()
     p = plan().c()
     fake = ctypes.c_void_p(0x10000)          # never dereferenced: validation fails first
@@ -110,6 +120,9 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     assert lib.spava_score_topk(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
     assert lib.spava_score_topk(ctypes.byref(p), odd, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
     assert lib.spava_score_topk(ctypes.byref(p), fake, fake, fake, fake, fake, 4, None) == S.SPAVA_EWORKSPACE
+    # scores may be NULL (they then live in the workspace, which must hold them)
+    need = lib.spava_score_topk_ws_bytes(ctypes.byref(p))
+    assert lib.spava_score_topk(ctypes.byref(p), fake, fake, None, fake, fake, need - 1, None) == S.SPAVA_EWORKSPACE
     assert lib.spava_gather_passing(ctypes.byref(p), fake, None, fake, fake, fake, None) == S.SPAVA_EINVAL
     assert lib.spava_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
                               fake, 1 << 20, None) == S.SPAVA_EINVAL
@@ -128,8 +141,11 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     # Context selector: same checks as the query selector, its own workspace size.
     assert lib.spava_score_topk_context(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
     assert lib.spava_score_topk_context(ctypes.byref(p), odd, fake, fake, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+    # (scores = NULL: the workspace must also hold the scores, so need - 1
+    # fails the check before anything is launched)
     need = lib.spava_score_topk_context_ws_bytes(ctypes.byref(p))
-    assert lib.spava_score_topk_context(ctypes.byref(p), fake, fake, fake, fake, fake, need - 1, None) == S.SPAVA_EWORKSPACE
+    assert lib.spava_score_topk_context(ctypes.byref(p), fake, fake, None, fake, fake, need - 1, None) == S.SPAVA_EWORKSPACE
+    assert lib.spava_score_topk_context(ctypes.byref(p), fake, fake, fake, fake, fake, 16, None) == S.SPAVA_EWORKSPACE
     assert b"spava_score_topk_context" in lib.spava_last_error()
     # Overlap: bad sizes, NULL or misaligned pointers; nothing to do succeeds.
     assert lib.spava_kv_overlap(-1, 4, fake, fake, fake, None) == S.SPAVA_EINVAL

@@ -153,3 +153,26 @@ def test_bitwise_determinism():
         t1, t2 = getattr(b1, name), getattr(b2, name)
         assert torch.equal(t1.view(torch.uint8) if t1.dtype == torch.bfloat16 else t1,
                            t2.view(torch.uint8) if t2.dtype == torch.bfloat16 else t2), name
+
+
+def test_scores_may_be_null():
+    # Without a scores buffer the selection is the same (scores live in ws).
+    w = W.small_workload("bf16", Hq=8, Hkv=2, d=128, la=40, V=3, L=300, n_q=24, lp=50, seed=23)
+    x = W.make_inputs(w)
+    plan = S.plan_for(w)
+    q, k, _ = dev_inputs(x, w)
+    ws = torch.empty(S.spava_score_topk_ws_bytes(plan), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((w.n_hosts, w.n_kv_heads, w.host_len), dtype=torch.float32, device="cuda")
+    idx_a = torch.empty((w.n_hosts, w.n_kv_heads, w.lp), dtype=torch.int32, device="cuda")
+    idx_b = torch.empty_like(idx_a)
+    S.spava_score_topk(plan, q, k, scores, idx_a, ws)
+    S.spava_score_topk(plan, q, k, None, idx_b, ws)
+    ctx_ws = torch.empty(S.spava_score_topk_context_ws_bytes(plan), dtype=torch.uint8, device="cuda")
+    idx_c = torch.empty_like(idx_a)
+    S.spava_score_topk_context(plan, q, k, None, idx_c, ctx_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b)
+    sc = O.block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
+    check_idx(sc, idx_b.cpu().numpy(), O.select_passing(sc, w.lp), w.lp)
+    scc = O.context_block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
+    check_idx(scc, idx_c.cpu().numpy(), O.select_passing(scc, w.lp), w.lp)
