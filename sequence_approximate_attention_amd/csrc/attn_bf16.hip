@@ -63,17 +63,6 @@ struct Geo {
   static constexpr int VINST = VBYTES / 1024 / kPairs;
 };
 
-__device__ __forceinline__ int wave_reduce_min(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ int wave_reduce_max(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
-}
-
 // The unit's key runs as scalar fields (selected by value, never by a
 // dynamic index, so that they stay in scalar registers).
 struct SegRun {
@@ -625,7 +614,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char sP[2 * kPairs * kPBytes];
   __shared__ float sAlpha[2 * kPairs * 64];
   __shared__ int sFlag[2 * kPairs];
-  __shared__ int sTok[2 * kWaves];
   __shared__ float sL[kPairs * 64];
 
   const int tid = threadIdx.x;
@@ -647,26 +635,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) row[qb] = unit_row(a, u, u.tile * kBM + pair * kWaveRows + 32 * qb + col);
 
-  // Token range of the workgroup (tile count, mask-free prefix).
-  int tmin = 0x7fffffff, tmax = -1;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-    if (row[qb].valid) {
-      tmin = min(tmin, row[qb].tok);
-      tmax = max(tmax, row[qb].tok);
+  // Token range of the workgroup (tile count, mask-free prefix), from the
+  // unit's row range: rows r of a context or anchor unit are tokens base + r;
+  // query rows r are tokens q0 + r % nq.
+  int gmin, gmax;
+  {
+    const int r_lo = u.tile * kBM;
+    if (u.kind == kAnchor || u.kind == kContext) {
+      const int base = (u.kind == kAnchor) ? 0 : a.la + u.host * a.L;
+      const int n = (u.kind == kAnchor) ? a.la : a.L;
+      gmin = base + r_lo;
+      gmax = base + min(n, r_lo + kBM) - 1;
+    } else {
+      const int q0 = a.la + a.V * a.L;
+      const int r_hi = min(a.nq * a.G, r_lo + kBM) - 1;
+      const bool wraps = r_hi - r_lo + 1 >= a.nq || r_lo % a.nq > r_hi % a.nq;
+      gmin = q0 + (wraps ? 0 : r_lo % a.nq);
+      gmax = q0 + (wraps ? a.nq - 1 : r_hi % a.nq);
     }
-  tmin = wave_reduce_min(tmin);
-  tmax = wave_reduce_max(tmax);
-  if (lane == 0) {
-    sTok[wave] = tmax;
-    sTok[kWaves + wave] = tmin;
-  }
-  __syncthreads();
-  int gmax = sTok[0], gmin = sTok[kWaves];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    gmax = max(gmax, sTok[w]);
-    gmin = min(gmin, sTok[kWaves + w]);
+    gmin = uni(gmin);
+    gmax = uni(gmax);
   }
   auto tiles = [&](SegRun& x) {
     int n = x.len;
