@@ -266,6 +266,8 @@ def main():
         stage["attn_fwd"].append(attn_ms_i)
         stage["lse_merge"].append(ev[3].elapsed_time(ev[4]))
     stage_ms = {kk: float(np.mean(vv)) for kk, vv in stage.items()}
+    # Per-step GPU time from the events (the four calls back to back).
+    step_ev = [sum(stage[kk][i] for kk in stage) for i in range(args.steps)]
     attn_ms = stage_ms["attn_fwd"]
     F_attn = attn_flops(wl)
     achieved = F_attn / (attn_ms * 1e-3) / 1e12
@@ -295,6 +297,7 @@ def main():
         "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,
         "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
         "stage_ms": stage_ms,
+        "step_event_ms": {"median": float(np.median(step_ev)), "min": float(np.min(step_ev))},
         # HBM-bound stages: algorithmic bytes / HIP-event time.
         "hbm_gbps": {
             "gather": 4.0 * wl.n_hosts * wl.n_kv_heads * wl.lp * wl.head_dim * 2 / (stage_ms["gather"] * 1e-3) / 1e9,
