@@ -176,3 +176,25 @@ def test_scores_may_be_null():
     check_idx(sc, idx_b.cpu().numpy(), O.select_passing(sc, w.lp), w.lp)
     scc = O.context_block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
     check_idx(scc, idx_c.cpu().numpy(), O.select_passing(scc, w.lp), w.lp)
+
+
+@pytest.mark.parametrize("lp", [0, 37, 256])
+def test_exact_rows_match_the_dense_plan_on_gpu(lp):
+    # Anchor, host-0 and query rows see their whole prefix, so the
+    # approximate run and the library's own dense plan (one host over the
+    # same N tokens) agree there for any lp; with lp = L every row agrees.
+    w = W.small_workload("bf16", Hq=8, Hkv=2, d=128, la=90, V=3, L=256, n_q=40, lp=lp, seed=29)
+    x = W.make_inputs(w)
+    plan, approx = run_full(w, x)
+    N = w.n_tokens
+    dense_plan = S.Plan(0, 1, N, 0, w.n_q_heads, w.n_kv_heads, w.head_dim, 0, S.SPAVA_BF16)
+    q, k, v = dev_inputs(x, w)
+    dense = S.prefill(dense_plan, q, k, v)
+    torch.cuda.synchronize()
+    L, la = w.host_len, w.n_anchor
+    rows = np.r_[0:la + L, la + w.n_hosts * L:N] if lp < L else np.arange(N)
+    tol = TOL["bf16"]
+    check_close(np64(approx.o)[rows], np64(dense.o)[rows], tol["o_max"], tol["o_mean"], "O vs dense plan")
+    check_close(np64(approx.lse)[:, rows], np64(dense.lse)[:, rows], tol["lse_max"], None, "LSE vs dense plan")
+    od, ld = O.dense_causal(x["q"], x["k"], x["v"])
+    check_close(np64(dense.o), od, tol["o_max"], tol["o_mean"], "dense plan O vs oracle")
