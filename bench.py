@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen2.5vl3b_32k")
     ap.add_argument("--lp", type=int, default=None, help="override the workload's passing length")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the library's dense causal plan over the workload's tokens and heads "
+                         "(one host of N tokens, no anchor, query or passing blocks) instead")
     ap.add_argument("--order", choices=("one-pass", "partials-first"), default="one-pass",
                     help="one-pass: score, gather, one attention call; partials-first: the rows "
                          "that need no passing block first, scores from the query partials' LSEs, "
@@ -173,7 +176,9 @@ def main():
     wl = {w.name: w for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS}[args.workload]
     if args.lp is not None:
         wl = wl.with_(lp=args.lp)
-    x = W.make_inputs(wl)
+    x = W.make_inputs(wl)   # the dense plan runs over the same tokens
+    if args.dense:
+        wl = wl.with_(name=wl.name + "_dense", n_anchor=0, n_hosts=1, host_len=wl.n_tokens, n_query=0, lp=0)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     plan = S.plan_for(wl)
@@ -292,7 +297,7 @@ def main():
                    "selector": args.selector, "order": args.order},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(wl.name) if args.lp is None else None},
+                     "traffic": measured_traffic(wl.name) if args.lp is None and not args.dense else None},
         "attn_tflop_per_launch": F_attn / 1e12,
         "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,
         "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
@@ -306,7 +311,7 @@ def main():
         },
         "cold_cache": cold,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.dense:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.selector)
     print(json.dumps(out), flush=True)
 
