@@ -160,6 +160,10 @@ def main():
                     help="after the timed loop, this many more steps each preceded (untimed) by a "
                          "512 MiB write that evicts the inputs from L2 and the Infinity Cache; "
                          "reported as cold_cache, not in value")
+    ap.add_argument("--no-dense-context", action="store_true",
+                    help="skip the six launches of the dense causal plan that are reported as "
+                         "context (profiled runs use it so that every attention dispatch is the "
+                         "workload's own)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -265,7 +269,7 @@ def main():
     # library (one host of N tokens), the one-GPU analogue of the pages'
     # speedups over FlashAttention.
     dense_ms = None
-    if not args.dense and args.order == "one-pass":
+    if not args.dense and not args.no_dense_context and args.order == "one-pass":
         dplan = S.Plan(0, 1, wl.n_tokens, 0, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 0, plan.dtype)
         db = S.alloc_buffers(dplan, dev)
         d_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
