@@ -31,8 +31,9 @@
  *     and ws are DEVICE pointers owned by the caller.  The library never
  *     allocates, frees or synchronises; every call only enqueues work on
  *     `stream` (a hipStream_t; NULL = the null stream) and returns.
- *   - All tensors are dense and row-major in the layouts stated below, and
- *     must be 16-byte aligned.
+ *   - Tensors are row-major in the layouts stated below and must be 16-byte
+ *     aligned.  Outputs are always dense; q, k and v follow the plan's
+ *     strides (dense when they are 0).
  *   - Return value: SPAVA_OK or an error code.  Argument checks run on the
  *     host before anything is enqueued; on an error nothing is enqueued and
  *     spava_last_error() (per thread) describes it.  A launch failure
