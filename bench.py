@@ -177,7 +177,7 @@ def main():
     import sequence_approximate_attention_amd as S
     import workloads as W
 
-    wl = {w.name: w for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS}[args.workload]
+    wl = {w.name: w for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS + [W.QWEN3B_32K_PAGE_DEFAULTS_Q128]}[args.workload]
     if args.lp is not None:
         wl = wl.with_(lp=args.lp)
     x = W.make_inputs(wl)   # the dense plan runs over the same tokens
