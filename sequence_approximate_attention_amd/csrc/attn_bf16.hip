@@ -402,7 +402,9 @@ __device__ __forceinline__ bool soft_probs(const Scores& sp, char* pwrite, const
 // common path needs no row maxima at all.  Then (rarely) the row maxima of
 // S(i-1) move the reference, the row sums are rescaled, P(i-1) is recomputed
 // and written again, and the output wave rescales O before adding it.
-template <int D, bool MASK>
+// LIVE = false is iteration T of a T-tile walk: S(T) would be read by nobody,
+// so it is not computed (no K reads, no MFMAs); it is left at -inf.
+template <int D, bool MASK, bool LIVE = true>
 __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __restrict__ kread,
                                           char* __restrict__ pwrite, float* __restrict__ awrite,
                                           int* __restrict__ fwrite, const SoftCtx<D>& cx, SoftState& st,
@@ -431,17 +433,21 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   float acc[2] = {0.0f, 0.0f};
   bf16x8 pb;
   bf16x8 ring[RING];
+  if (LIVE) {
 #pragma unroll
-  for (int n = 0; n < RING; ++n) ring[n] = kfrag(n);
+    for (int n = 0; n < RING; ++n) ring[n] = kfrag(n);
+  }
 #pragma unroll
   for (int n = 0; n < NA; ++n) {
-    const bf16x8 af = ring[n % RING];
-    if (n + RING < NA) ring[n % RING] = kfrag(n + RING);
     const int h2 = n % 2, c = n / 2;
+    if (LIVE) {
+      const bf16x8 af = ring[n % RING];
+      if (n + RING < NA) ring[n % RING] = kfrag(n + RING);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-      s_new.s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          af, cx.qf[qb][c], c == 0 ? f32x16{} : s_new.s[qb][h2], 0, 0, 0);
+      for (int qb = 0; qb < 2; ++qb)
+        s_new.s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            af, cx.qf[qb][c], c == 0 ? f32x16{} : s_new.s[qb][h2], 0, 0, 0);
+    }
 #pragma unroll
     for (int t = 0; t < PPC; ++t) {
       const int idx = n * PPC + t;
@@ -483,9 +489,17 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   }
   if (cx.lane == 0) *fwrite = moved;
 
+  if (!LIVE) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_new.s[qb][h2][e] = -INFINITY;
+  }
   // Visibility of S(i): keys past the run's end, or in a causal run past the
   // row's token, get -inf.
-  if (MASK) {
+  if (MASK && LIVE) {
     const TileRef tr = tile_ref(run, i);
     const SegRun& sr = tr.run;
 #pragma unroll
@@ -722,11 +736,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
       soft_iter<D, false>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
       soft_iter<D, false>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
     }
-    for (int i = n_plain; i < n_iter; i += 2) {
+    for (int i = n_plain; i < run.T; i += 2) {
       soft_iter<D, true>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
-      if (i + 1 >= n_iter) break;
+      if (i + 1 >= run.T) break;
       soft_iter<D, true>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
     }
+    // Iteration T computes P(T-1) only; in iteration T+1 (the output wave's
+    // last P V) this wave has nothing left that is read, so it only meets the
+    // barrier.
+    if ((run.T & 1) == 0)
+      soft_iter<D, true, false>(run.T, run, knext(), p1, a1, f1, cx, st, sA, sB);
+    else
+      soft_iter<D, true, false>(run.T, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    __syncthreads();
     // Row sums to the output wave; LSE out.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
