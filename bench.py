@@ -90,13 +90,14 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(w, x, selector="query"):
+def cpu_baseline(w, x, selector="query", attn_budget_s=8.0):
     """The oracle as it stands, on a bounded sample of the same layer:
-    scoring + selection in full, then the context rows of hosts 0 and V-1
-    for the query heads of one KV group; the attention time is extrapolated
-    to the whole layer by its share of attention pairs.  With the context
-    selector the scoring is timed on block 0 and KV head 0 and extrapolated
-    to all V * Hkv lists."""
+    scoring + selection in full, then the context rows of (host, KV group)
+    pairs in a fixed spread order (hosts 0 and V-1 of group 0 first) until
+    about `attn_budget_s` seconds of attention have been timed; the attention
+    time is extrapolated to the whole layer by its share of attention pairs.
+    With the context selector the scoring is timed on block 0 and KV head 0
+    and extrapolated to all V * Hkv lists."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -117,10 +118,20 @@ def cpu_baseline(w, x, selector="query"):
     idx = O.select_passing(sc, lp)
     kp, vp = O.gather_passing(x["k"], x["v"], idx, la, L)
     t1 = time.perf_counter()
-    for h in (0, V - 1):                    # the query heads of KV group 0
-        O.context_rows(x["q"][:, :G], x["k"][:, :1], x["v"][:, :1], kp[:1], vp[:1], la, V, L, h, scale)
+    hosts = []
+    for h in [0, V - 1, V // 2, V // 4, 3 * V // 4] + list(range(V)):
+        if h not in hosts:
+            hosts.append(h)
+    order = [(h, g) for g in range(w.n_kv_heads) for h in hosts]
+    done = []
+    for h, g in order:
+        if len(done) >= 2 and time.perf_counter() - t1 >= attn_budget_s:
+            break
+        O.context_rows(x["q"][:, g * G:(g + 1) * G], x["k"][:, g:g + 1], x["v"][:, g:g + 1], kp[g:g + 1],
+                       vp[g:g + 1], la, V, L, h, scale)
+        done.append((h, g))
     t2 = time.perf_counter()
-    sample_pairs = G * sum(L * (la + h * lp) + L * (L + 1) // 2 for h in (0, V - 1))
+    sample_pairs = G * sum(L * (la + h * lp) + L * (L + 1) // 2 for h, _ in done)
     total_pairs = attn_pairs_per_head(w) * w.n_q_heads
     t_select = (t1 - t0) + t_extra
     t_layer = t_select + (t2 - t1) * total_pairs / sample_pairs
@@ -132,7 +143,8 @@ def cpu_baseline(w, x, selector="query"):
         "sample": (f"float64 numpy oracle: {selector} scores+top-lp+gather of the full layer ({t_select:.1f} s"
                    + (", context scores of one of the V*Hkv lists timed and extrapolated" if selector == "context" else "")
                    + "), "
-                   f"then context rows of hosts 0 and {V - 1} for {G} of {w.n_q_heads} query heads "
+                   f"then the context rows of {len(done)} (host, KV group) pairs "
+                   f"({', '.join(f'{h}/{g}' for h, g in done)}; {G} query heads each) "
                    f"({t2 - t1:.1f} s); attention extrapolated by pair count "
                    f"({total_pairs / sample_pairs:.1f}x) to {t_layer:.1f} s per layer"),
     }
