@@ -404,7 +404,10 @@ __device__ __forceinline__ bool soft_probs(const Scores& sp, char* pwrite, const
 // and written again, and the output wave rescales O before adding it.
 // LIVE = false is iteration T of a T-tile walk: S(T) would be read by nobody,
 // so it is not computed (no K reads, no MFMAs); it is left at -inf.
-template <int D, bool MASK, bool LIVE = true>
+// HEAD = 1 is iteration 0: there is no P(-1), only S(0) is computed.  HEAD = 2
+// is iteration 1: no row has a reference yet, so P(0) is computed once,
+// against S(0)'s own row maxima, instead of speculatively and again.
+template <int D, bool MASK, bool LIVE = true, int HEAD = 0>
 __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __restrict__ kread,
                                           char* __restrict__ pwrite, float* __restrict__ awrite,
                                           int* __restrict__ fwrite, const SoftCtx<D>& cx, SoftState& st,
@@ -448,46 +451,52 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
         s_new.s[qb][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             af, cx.qf[qb][c], c == 0 ? f32x16{} : s_new.s[qb][h2], 0, 0, 0);
     }
+    if (HEAD == 0) {
 #pragma unroll
-    for (int t = 0; t < PPC; ++t) {
-      const int idx = n * PPC + t;
-      const int qb = idx >> 5, kc = (idx >> 3) & 3, e = idx & 7;
-      const float p = __builtin_amdgcn_exp2f(fmaf(s_prev.s[qb][kc >> 1][8 * (kc & 1) + e], cx.sl2, -mu[qb]));
-      acc[qb] += p;
-      pb[e] = (__bf16)p;
-      if (e == 7) *(bf16x8*)(pwrite + p_off(qb, kc, cx.lane)) = pb;
+      for (int t = 0; t < PPC; ++t) {
+        const int idx = n * PPC + t;
+        const int qb = idx >> 5, kc = (idx >> 3) & 3, e = idx & 7;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s_prev.s[qb][kc >> 1][8 * (kc & 1) + e], cx.sl2, -mu[qb]));
+        acc[qb] += p;
+        pb[e] = (__bf16)p;
+        if (e == 7) *(bf16x8*)(pwrite + p_off(qb, kc, cx.lane)) = pb;
+      }
     }
   }
-  bool grow = false;
+  if (HEAD != 1) {
+    bool grow = HEAD == 2;
+    if (HEAD == 0) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) grow |= !(acc[qb] <= 256.0f) || st.m[qb] == -INFINITY;
-  int moved = 0;
-  float alpha[2] = {1.0f, 1.0f};
-  if (__any(grow)) {
-    moved = 1;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float x;
-      asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(x));   // -inf, computed only here
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x = fmaxf(x, s_prev.s[qb][h2][e]);
-      const float mp = fmaxf(x, __shfl_xor(x, 32)) * cx.sl2;
-      const float m_new = fmaxf(st.m[qb], mp);
-      alpha[qb] = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m[qb] - m_new);
-      st.m[qb] = m_new;
-      st.l[qb] *= alpha[qb];
+      for (int qb = 0; qb < 2; ++qb) grow |= !(acc[qb] <= 256.0f) || st.m[qb] == -INFINITY;
     }
-    soft_probs<D>(s_prev, pwrite, cx, st, acc);
-  }
-  st.l[0] += acc[0];   // float32 row sums: the LSE output needs them to ~1e-6
-  st.l[1] += acc[1];
-  if (cx.hi == 0) {
+    int moved = 0;
+    float alpha[2] = {1.0f, 1.0f};
+    if (__any(grow)) {
+      moved = 1;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) awrite[qb * 32 + (cx.lane & 31)] = alpha[qb];
+      for (int qb = 0; qb < 2; ++qb) {
+        float x;
+        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(x));   // -inf, computed only here
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x = fmaxf(x, s_prev.s[qb][h2][e]);
+        const float mp = fmaxf(x, __shfl_xor(x, 32)) * cx.sl2;
+        const float m_new = fmaxf(st.m[qb], mp);
+        alpha[qb] = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m[qb] - m_new);
+        st.m[qb] = m_new;
+        st.l[qb] *= alpha[qb];
+      }
+      soft_probs<D>(s_prev, pwrite, cx, st, acc);
+    }
+    st.l[0] += acc[0];   // float32 row sums: the LSE output needs them to ~1e-6
+    st.l[1] += acc[1];
+    if (cx.hi == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) awrite[qb * 32 + (cx.lane & 31)] = alpha[qb];
+    }
+    if (cx.lane == 0) *fwrite = moved;
   }
-  if (cx.lane == 0) *fwrite = moved;
 
   if (!LIVE) {
 #pragma unroll
@@ -732,11 +741,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     int* const f0 = sFlag + pair;
     int* const f1 = sFlag + kPairs + pair;
     const int n_plain = min(unmasked_prefix(run, gmin), n_iter) & ~1;
-    for (int i = 0; i < n_plain; i += 2) {
+    // Iterations 0 and 1: S(0) alone, then S(1) with P(0) against S(0)'s
+    // maxima (a walk of one tile makes iteration 1 its last, dead one).
+    if (n_plain >= 2) {
+      soft_iter<D, false, true, 1>(0, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, false, true, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    } else {
+      soft_iter<D, true, true, 1>(0, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      if (run.T >= 2)
+        soft_iter<D, true, true, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+      else
+        soft_iter<D, true, false, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    }
+    for (int i = 2; i < n_plain; i += 2) {
       soft_iter<D, false>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
       soft_iter<D, false>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
     }
-    for (int i = n_plain; i < run.T; i += 2) {
+    for (int i = max(2, n_plain); i < run.T; i += 2) {
       soft_iter<D, true>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
       if (i + 1 >= run.T) break;
       soft_iter<D, true>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
@@ -744,10 +765,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     // Iteration T computes P(T-1) only; in iteration T+1 (the output wave's
     // last P V) this wave has nothing left that is read, so it only meets the
     // barrier.
-    if ((run.T & 1) == 0)
-      soft_iter<D, true, false>(run.T, run, knext(), p1, a1, f1, cx, st, sA, sB);
-    else
-      soft_iter<D, true, false>(run.T, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    if (run.T >= 2) {
+      if ((run.T & 1) == 0)
+        soft_iter<D, true, false>(run.T, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      else
+        soft_iter<D, true, false>(run.T, run, knext(), p0, a0, f0, cx, st, sB, sA);
+    }
     __syncthreads();
     // Row sums to the output wave; LSE out.
 #pragma unroll
