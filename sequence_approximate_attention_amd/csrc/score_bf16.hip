@@ -259,7 +259,7 @@ constexpr int kCsKbCtx = 3;                      // ... context selector
 constexpr int kCsRows = 32;                      // rows per chunk
 constexpr int kCsSlots = 3;                      // Q tile ring per half
 constexpr int kCsLseRows = 4096;                 // rows of the LSE table per pass
-constexpr int kMaxKeyChunks = 16;                // key chunks per block (L <= 8192)
+constexpr int kMaxKeyChunks = 16;                // key chunks per block (past 8192 keys, chunks grow)
 
 template <int D>
 struct CsGeo {
