@@ -138,6 +138,11 @@ __device__ int block_exclusive_scan(int x, int* sWave, int* total) {
   return res;
 }
 
+// Each thread owns the contiguous keys [j0, j1) of the list, so the kept
+// indices come out in index order.  With NPT > 0 (lists of at most
+// NPT * kTopkThreads keys) the thread reads its keys from memory once and
+// every pass below works on registers; NPT = 0 reads them again per pass.
+template <int NPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
                                                             int32_t* __restrict__ idx, int L, int lp) {
   __shared__ int sHist[256];
@@ -147,14 +152,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const float* sc = scores + (long)blockIdx.x * L;
   int32_t* out = idx + (long)blockIdx.x * lp;
 
+  const int chunk = (L + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = min(L, tid * chunk), j1 = min(L, j0 + chunk);
+  const int n = j1 - j0;
+  constexpr int NR = NPT > 0 ? NPT : 1;
+  uint32_t cache[NR];
+  if (NPT > 0) {
+#pragma unroll
+    for (int e = 0; e < NR; ++e) {
+      const uint32_t u = order_key(sc[min(j0 + e, L - 1)]);   // in the list even past its end
+      cache[e] = (e < n) ? u : 0u;
+    }
+  }
+  auto key = [&](int e) -> uint32_t { return NPT > 0 ? cache[e] : order_key(sc[j0 + e]); };
+  const int n_loop = NPT > 0 ? NPT : n;
+
   // Radix select of the lp-th largest order key, 8 bits at a time.
   uint32_t prefix = 0, pmask = 0;
   int need = lp;  // rank still to find among keys matching prefix
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) sHist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < L; j += kTopkThreads) {
-      const uint32_t u = order_key(sc[j]);
+#pragma unroll
+    for (int e = 0; e < n_loop; ++e) {
+      if (e >= n) break;
+      const uint32_t u = key(e);
       if ((u & pmask) == prefix) atomicAdd(&sHist[(u >> shift) & 255], 1);
     }
     __syncthreads();
@@ -194,32 +216,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const uint32_t thr = prefix;  // order key of the lp-th largest score
   const int take_eq = need;     // keys equal to thr that are kept (lowest indices)
 
-  // Contiguous chunk per thread so the output comes out in index order.
-  const int chunk = (L + kTopkThreads - 1) / kTopkThreads;
-  const int j0 = min(L, tid * chunk), j1 = min(L, j0 + chunk);
   int n_eq = 0;
-  for (int j = j0; j < j1; ++j) n_eq += (order_key(sc[j]) == thr);
+#pragma unroll
+  for (int e = 0; e < n_loop; ++e) {
+    if (e >= n) break;
+    n_eq += (key(e) == thr);
+  }
   int eq_total;
   int eq_before = block_exclusive_scan(n_eq, sWave, &eq_total);
   int n_sel = 0;
   {
-    int e = eq_before;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = order_key(sc[j]);
+    int q = eq_before;
+#pragma unroll
+    for (int e = 0; e < n_loop; ++e) {
+      if (e >= n) break;
+      const uint32_t u = key(e);
       if (u > thr) ++n_sel;
-      else if (u == thr) { if (e < take_eq) ++n_sel; ++e; }
+      else if (u == thr) { if (q < take_eq) ++n_sel; ++q; }
     }
   }
   int sel_total;
   int pos = block_exclusive_scan(n_sel, sWave, &sel_total);
   {
-    int e = eq_before;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = order_key(sc[j]);
+    int q = eq_before;
+#pragma unroll
+    for (int e = 0; e < n_loop; ++e) {
+      if (e >= n) break;
+      const uint32_t u = key(e);
       bool keep = false;
       if (u > thr) keep = true;
-      else if (u == thr) { keep = e < take_eq; ++e; }
-      if (keep) out[pos++] = j;
+      else if (u == thr) { keep = q < take_eq; ++q; }
+      if (keep) out[pos++] = j0 + e;
     }
   }
 }
@@ -312,7 +339,15 @@ hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s) {
 
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s) {
   if (n_lists == 0 || lp == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
+  const int chunk = (L + kTopkThreads - 1) / kTopkThreads;
+  if (chunk <= 4)
+    hipLaunchKernelGGL(topk_kernel<4>, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
+  else if (chunk <= 8)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
+  else if (chunk <= 16)
+    hipLaunchKernelGGL(topk_kernel<16>, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
+  else
+    hipLaunchKernelGGL(topk_kernel<0>, dim3(n_lists), dim3(kTopkThreads), 0, s, scores, idx, L, lp);
   return hipGetLastError();
 }
 

@@ -198,3 +198,24 @@ def test_exact_rows_match_the_dense_plan_on_gpu(lp):
     check_close(np64(approx.lse)[:, rows], np64(dense.lse)[:, rows], tol["lse_max"], None, "LSE vs dense plan")
     od, ld = O.dense_causal(x["q"], x["k"], x["v"])
     check_close(np64(dense.o), od, tol["o_max"], tol["o_mean"], "dense plan O vs oracle")
+
+
+@pytest.mark.parametrize("L,lp", [(1000, 333), (5000, 700), (9000, 64), (16384, 4096), (17000, 300)])
+def test_selection_across_list_lengths(L, lp):
+    # The top-lp kernel keeps up to 4, 8 or 16 keys per thread in registers
+    # (lists of up to 4096, 8192, 16384 keys) and reads longer lists again
+    # per pass; every size class against the oracle's scores and selection.
+    w = W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=0, V=1, L=L, n_q=6, lp=lp, seed=31)
+    x = W.make_inputs(w)
+    plan = S.plan_for(w)
+    q, k, _ = dev_inputs(x, w)
+    ws = torch.empty(S.spava_score_topk_ws_bytes(plan), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((w.n_hosts, w.n_kv_heads, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.n_hosts, w.n_kv_heads, lp), dtype=torch.int32, device="cuda")
+    S.spava_score_topk(plan, q, k, scores, idx, ws)
+    torch.cuda.synchronize()
+    want = O.block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
+    got = np64(scores)
+    err = np.abs(got - want) / np.maximum(np.abs(want), 1e-30)
+    assert err.max() < 1e-5, f"scores rel err {err.max():.2e}"
+    check_idx(want, idx.cpu().numpy(), O.select_passing(want, lp), lp)
