@@ -38,7 +38,6 @@ namespace spava {
 namespace {
 
 constexpr int kBN = kKeyTile;
-constexpr float kGrowLog2 = 8.0f;
 
 // ---------------------------------------------------------------------------
 // Row statistics over key chunks.
@@ -216,25 +215,35 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
             if (j >= lim[qb]) s[qb][h2][e] = -INFINITY;
           }
     }
+    // The sums are taken against the running reference m as long as no term
+    // can exceed 2^8 (a lane's sum of its 32 terms bounds each of them), so
+    // the common tile needs no row maximum; otherwise (and while a row has
+    // no reference yet) the tile's maxima move m and the sum is taken again.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][h2][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      if (__any(mx > m[qb] + kGrowLog2)) {
-        const float m_new = fmaxf(m[qb], mx);
-        l[qb] *= (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qb] - m_new);
-        m[qb] = m_new;
-      }
       const float m_use = (m[qb] == -INFINITY) ? 0.0f : m[qb];
       float psum = 0.0f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) psum += __builtin_amdgcn_exp2f(fmaf(s[qb][h2][e], sl2, -m_use));
+      if (__any(!(psum <= 256.0f) || m[qb] == -INFINITY)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][h2][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        const float m_new = fmaxf(m[qb], mx);
+        l[qb] *= (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qb] - m_new);
+        m[qb] = m_new;
+        const float m_use2 = (m_new == -INFINITY) ? 0.0f : m_new;
+        psum = 0.0f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) psum += __builtin_amdgcn_exp2f(fmaf(s[qb][h2][e], sl2, -m_use2));
+      }
       l[qb] += psum;
     }
   }
