@@ -338,8 +338,16 @@ def main():
         "score_tflops": score_flops(wl, args.selector) / (stage_ms["score_topk"] * 1e-3) / 1e12,
         "stage_ms": stage_ms,
         "step_event_ms": {"median": float(np.median(step_ev)), "min": float(np.min(step_ev))},
-        # HBM-bound stages: algorithmic bytes / HIP-event time.
+        # HBM-bound stages: algorithmic bytes / HIP-event time.  The scoring
+        # call (MFMA- and exp-bound, listed for completeness) reads every
+        # block's keys and the scoring rows' Q once and writes the scores and
+        # the indices.
         "hbm_gbps": {
+            "score_topk": (wl.n_hosts * wl.host_len * wl.n_kv_heads * wl.head_dim * 2
+                           + (wl.n_query if args.selector == "query" else wl.n_hosts * wl.host_len)
+                           * wl.n_q_heads * wl.head_dim * 2
+                           + wl.n_hosts * wl.n_kv_heads * (wl.host_len + wl.lp) * 4)
+                          / (stage_ms["score_topk"] * 1e-3) / 1e9,
             "gather": 4.0 * wl.n_hosts * wl.n_kv_heads * wl.lp * wl.head_dim * 2 / (stage_ms["gather"] * 1e-3) / 1e9,
             "lse_merge": ((wl.n_hosts + 1) * wl.n_query * wl.n_q_heads * (wl.head_dim + 1) * 4
                           + wl.n_query * wl.n_q_heads * (wl.head_dim * 2 + 4)) / (stage_ms["lse_merge"] * 1e-3) / 1e9,
