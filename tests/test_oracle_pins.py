@@ -436,3 +436,37 @@ def test_context_selection_can_differ_from_query_selection():
     assert ctx[0, 0].tolist() == [0] and qry[0, 0].tolist() == [5]
     assert O.kv_overlap(ctx, qry)[0, 0] == 0
     assert O.kv_overlap(ctx, ctx)[0, 0] == 1
+
+
+@pytest.mark.parametrize("lp", [2, 5, 16, 97])
+def test_kv_overlap_closed_forms(lp):
+    # The overlap is the size of the intersection of two key sets (APB-V
+    # review, "What would settle it"), so it is known without set code on
+    # lists whose common members follow from arithmetic:
+    #   even keys vs multiples of 3: the common keys are the multiples of 6
+    #     up to 2 (lp - 1), floor(2 (lp - 1) / 6) + 1 of them;
+    #   0..lp-1 vs 1..lp: all but one key are shared, none at equal positions;
+    #   a list against itself reversed in position order (still one set): lp;
+    #   disjoint halves (evens vs odds): 0.
+    # A position-wise comparison of the two lists fails the first two lines;
+    # a merge walk that assumes both lists ascending fails the third.
+    evens = np.arange(lp) * 2
+    threes = np.arange(lp) * 3
+    shifted_a = np.arange(lp)
+    shifted_b = np.arange(1, lp + 1)
+    odds = np.arange(lp) * 2 + 1
+    idx_a = np.stack([evens, shifted_a, evens, evens])[None].astype(np.int32)   # [1, 4, lp]
+    idx_b = np.stack([threes, shifted_b, evens[::-1], odds])[None].astype(np.int32)
+    got = O.kv_overlap(idx_a, idx_b)
+    assert got.shape == (1, 4)
+    assert got[0].tolist() == [(2 * (lp - 1)) // 6 + 1, lp - 1, lp, 0]
+
+
+def test_kv_overlap_small_hand_cases():
+    # [1, 2] and [2, 3] share key 2 only (position-wise they share nothing);
+    # [0, 5, 9] and [5, 9, 11] share 5 and 9 at shifted positions.
+    a = np.array([[[1, 2, 0], [0, 5, 9]]], dtype=np.int32)
+    b = np.array([[[2, 3, 7], [5, 9, 11]]], dtype=np.int32)
+    assert O.kv_overlap(a, b).tolist() == [[1, 2]]
+    # Symmetric in its two arguments.
+    assert O.kv_overlap(b, a).tolist() == [[1, 2]]
