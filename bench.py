@@ -6,8 +6,10 @@ spava_score_topk -> spava_gather_passing -> spava_attn_fwd -> spava_lse_merge
 (--order partials-first: the attention's LOCAL phase, scores from the query
 partials, gather, the PASSING phase, merge; --selector context: the
 context-driven selector in place of spava_score_topk).
-Workload: Qwen2.5-VL-3B-like attention at 32K tokens (16 query / 2 KV heads,
-d=128; anchor 2048; 8 virtual hosts x 3840; query 128; lp=1024), bf16.
+Default workload: Qwen2.5-VL-7B-like attention at 256K tokens (28 query / 4
+KV heads, d=128; anchor 4096; 32 virtual hosts x 8128 frame-structured
+tokens; query 512; lp=4096), bf16 -- the largest single-GPU configuration.
+--workload picks another (e.g. qwen2.5vl3b_32k).
 
 Prints ONE JSON line.  Besides the throughput it reports the roofline of the
 dominant call (the fused attention) from HIP events recorded on the stream
@@ -29,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "approx-attention prefill tokens/s per layer; TFLOP/s and % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X float32 vector ALUs (the float32 path does not use MFMA)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -57,7 +60,9 @@ def score_flops(w, selector="query") -> float:
     return 2.0 * w.head_dim * (w.n_query * w.n_q_heads) * (w.n_hosts * w.host_len)
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_qwen3b_32k_traffic.md")
+# Copy-calibrated FETCH_SIZE + WRITE_SIZE summaries of the attention kernel,
+# one per workload: profiles/attn_fwd_<workload>_traffic.md.
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # The attention kernel's sources: its file and the headers that define its
 # unit order and copy helpers.
 ATTN_SOURCES = [os.path.join(ROOT, "sequence_approximate_attention_amd", "csrc", f)
@@ -74,79 +79,128 @@ def attn_source_sha256():
 
 def measured_traffic(workload):
     """HBM-side bytes per attention launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was
-    taken on another workload or a different kernel source than the one built
-    here."""
+    of this workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when
+    there is none or it was taken on a different kernel source than the one
+    built here."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(TRAFFIC_DIR, "attn_fwd_*_traffic.md"))):
+        try:
+            fields = {}
+            for line in open(path):
+                if " = " in line:
+                    key, val = line.strip().split(" = ", 1)
+                    fields[key] = val
+            if fields.get("workload") != workload:
+                continue
+            if fields.get("kernel_source_sha256") != attn_source_sha256():
+                return None
+            return float(fields["traffic_bytes_per_launch"])
+        except (OSError, KeyError, ValueError):
+            continue
+    return None
+
+
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model name)."""
     try:
-        fields = {}
-        for line in open(TRAFFIC_SUMMARY):
-            if " = " in line:
-                key, val = line.strip().split(" = ", 1)
-                fields[key] = val
-        if fields.get("kernel_source_sha256") != attn_source_sha256() or fields.get("workload") != workload:
-            return None
-        return float(fields["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
 
 
-def cpu_baseline(w, x, selector="query", attn_budget_s=8.0):
-    """The oracle as it stands, on a bounded sample of the same layer:
-    scoring + selection in full, then the context rows of (host, KV group)
-    pairs in a fixed spread order (hosts 0 and V-1 of group 0 first) until
-    about `attn_budget_s` seconds of attention have been timed; the attention
-    time is extrapolated to the whole layer by its share of attention pairs.
-    With the context selector the scoring is timed on block 0 and KV head 0
-    and extrapolated to all V * Hkv lists."""
-    import oracle as O
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return 1
+
+
+def cpu_baseline(w, x, selector="query", attn_budget_s=10.0, row_stride=61):
+    """The oracle as it stands, on a bounded sample of the same layer.
+
+    Scoring, top-lp selection and the gather run in full (with the context
+    selector, the scores of one of the V * Hkv lists are timed and
+    extrapolated).  The attention then runs on a deterministic row sample:
+    every ``row_stride``-th token of a host (a prime, so every tile residue
+    is hit) with every query head, hosts taken in a spread order (0, V-1,
+    V/2, V/4, 3V/4, then the rest) until about ``attn_budget_s`` seconds have
+    been timed, plus every ``row_stride``-th query token (through its V+1
+    partials and the merge).  The attention time is extrapolated to the
+    whole layer by the ratio of visible (query, key) pairs: "sampled,
+    flop-extrapolated"."""
+    import oracle as O
     la, V, L, nq, lp = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.lp
+    Hq = w.n_q_heads
     scale = 1.0 / math.sqrt(w.head_dim)
     G = w.group
+    x32 = {n: x[n] for n in ("q", "k", "v")}
     t0 = time.perf_counter()
     t_extra = 0.0
     if selector == "context":
         sc = np.zeros((V, w.n_kv_heads, L))
-        sc[0, 0] = O.context_block_scores(x["q"][la:la + L, :G], x["k"][la:la + L, :1], 0, 1, L, 0, scale)[0, 0]
+        sc[0, 0] = O.context_block_scores(x32["q"][la:la + L, :G], x32["k"][la:la + L, :1], 0, 1, L, 0,
+                                          scale)[0, 0]
         t_extra = (time.perf_counter() - t0) * (V * w.n_kv_heads - 1)
     else:
-        sc = O.block_scores(x["q"], x["k"], la, V, L, nq)
+        sc = O.block_scores(x32["q"], x32["k"], la, V, L, nq)
     idx = O.select_passing(sc, lp)
-    kp, vp = O.gather_passing(x["k"], x["v"], idx, la, L)
+    kp, vp = O.gather_passing(x32["k"], x32["v"], idx, la, L)
     t1 = time.perf_counter()
+    threads = blas_threads()   # after the matrix products: the pool the oracle used
+
     hosts = []
     for h in [0, V - 1, V // 2, V // 4, 3 * V // 4] + list(range(V)):
         if h not in hosts:
             hosts.append(h)
-    order = [(h, g) for g in range(w.n_kv_heads) for h in hosts]
+    q0 = la + V * L
+    qrows = [(t, a) for t in range(q0, q0 + nq, row_stride) for a in range(Hq)]
+    sample_pairs = 0
+    # Query tokens: anchor + causal query prefix, then every block in full.
+    for t, _ in qrows:
+        sample_pairs += la + (t - q0 + 1) + V * L
+    O.sampled_rows(x32["q"], x32["k"], x32["v"], kp, vp, la, V, L, nq, qrows, scale)
     done = []
-    for h, g in order:
-        if len(done) >= 2 and time.perf_counter() - t1 >= attn_budget_s:
+    for h in hosts:
+        if done and time.perf_counter() - t1 >= attn_budget_s:
             break
-        O.context_rows(x["q"][:, g * G:(g + 1) * G], x["k"][:, g:g + 1], x["v"][:, g:g + 1], kp[g:g + 1],
-                       vp[g:g + 1], la, V, L, h, scale)
-        done.append((h, g))
+        b0 = la + h * L
+        rows = [(t, a) for t in range(b0, b0 + L, row_stride) for a in range(Hq)]
+        O.sampled_rows(x32["q"], x32["k"], x32["v"], kp, vp, la, V, L, nq, rows, scale)
+        sample_pairs += sum(la + h * lp + (t - b0) + 1 for t, _ in rows)
+        done.append(h)
     t2 = time.perf_counter()
-    sample_pairs = G * sum(L * (la + h * lp) + L * (L + 1) // 2 for h, _ in done)
-    total_pairs = attn_pairs_per_head(w) * w.n_q_heads
+    total_pairs = attn_pairs_per_head(w) * Hq
     t_select = (t1 - t0) + t_extra
     t_layer = t_select + (t2 - t1) * total_pairs / sample_pairs
+    nproc, model = host_cpu()
     return {
         "value": w.n_tokens / t_layer,
         "unit": "tokens/s",
-        "cores": int(cores),
+        "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle: {selector} scores+top-lp+gather of the full layer ({t_select:.1f} s"
-                   + (", context scores of one of the V*Hkv lists timed and extrapolated" if selector == "context" else "")
-                   + "), "
-                   f"then the context rows of {len(done)} (host, KV group) pairs "
-                   f"({', '.join(f'{h}/{g}' for h, g in done)}; {G} query heads each) "
-                   f"({t2 - t1:.1f} s); attention extrapolated by pair count "
-                   f"({total_pairs / sample_pairs:.1f}x) to {t_layer:.1f} s per layer"),
+        "nproc": nproc,
+        "cpu_model": model,
+        "sample": (f"sampled, flop-extrapolated. float64 numpy oracle on {threads} BLAS threads "
+                   f"({nproc} logical CPUs available, {model}): {selector} scores + top-lp + gather of "
+                   f"the full layer ({t_select:.1f} s"
+                   + (", context scores of one of the V*Hkv lists timed and extrapolated"
+                      if selector == "context" else "")
+                   + f"); attention of every {row_stride}th token with all {Hq} query heads of hosts "
+                   f"{', '.join(str(h) for h in done)} and every {row_stride}th query token "
+                   f"({len(qrows)} query rows through their {V + 1} partials) "
+                   f"({t2 - t1:.1f} s for {sample_pairs:.3g} of {total_pairs:.3g} visible pairs); "
+                   f"attention extrapolated by pair count ({total_pairs / sample_pairs:.0f}x) "
+                   f"to {t_layer:.1f} s per layer"),
     }
 
 
@@ -156,7 +210,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen2.5vl3b_32k")
+    ap.add_argument("--workload", default="qwen2.5vl7b_256k_frames")
     ap.add_argument("--lp", type=int, default=None, help="override the workload's passing length")
     ap.add_argument("--dense", action="store_true",
                     help="time the library's dense causal plan over the workload's tokens and heads "
@@ -198,7 +252,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     plan = S.plan_for(wl)
-    to = lambda n: torch.from_numpy(x[n + "16"].view(np.int16)).view(torch.bfloat16).to(dev)
+    if wl.dtype == "bf16":
+        to = lambda n: torch.from_numpy(x[n + "16"].view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        to = lambda n: torch.from_numpy(np.ascontiguousarray(x[n])).to(dev)
     q, k, v = to("q"), to("k"), to("v")
     bufs = S.alloc_buffers(plan, dev)
     if args.selector == "context":
@@ -312,6 +369,7 @@ def main():
     F_attn = attn_flops(wl)
     achieved = F_attn / (attn_ms * 1e-3) / 1e12
     tokens_per_s = wl.n_tokens / (ms_per_step * 1e-3)
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_VALU_TFLOPS
 
     out = {
         "metric": METRIC,
@@ -324,14 +382,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.n_tokens, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "anchor": wl.n_anchor,
                    "hosts": wl.n_hosts, "host_len": wl.host_len, "query": wl.n_query, "lp": wl.lp,
                    "selector": args.selector, "order": args.order},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(wl.name) if args.lp is None and not args.dense else None},
         "attn_tflop_per_launch": F_attn / 1e12,
         "step_tflops": (F_attn + score_flops(wl, args.selector)) / (ms_per_step * 1e-3) / 1e12,

@@ -132,7 +132,7 @@ size_t spava_score_topk_ws_bytes(const spava_plan* plan);
 
 /*
  * Step 1: block scores and top-lp selection.
- * Scoring rule (Figure 5 caption: Q_qr K^(h)T estimates KV importance): for
+ * Scoring rule (Figure 5 caption: query logits Q_qr K^(h)T rank block h): for
  * block h and KV head g,
  *     scores[h][g][j] = sum over query tokens i and query heads a of group g
  *                       of softmax_j( q[la+V*L+i][a] . k[la+h*L+j][g] * scale )

@@ -13,8 +13,8 @@ Source pages (cited by title and section/figure):
            Sequence-Parallelism-aware Approximate Attention" (sciencestack):
            abstract; Figure 2 caption (anchor block B_a, context blocks B^(h),
            passing blocks B_p, query block B_qr); Figure 3 caption (fused
-           context and query forward); Figure 5 caption (Q_qr K^(h)T estimates
-           KV importance; query attention and its merging).
+           context and query forward); Figure 5 caption (the query block's
+           logits against block h rank its keys; query attention and its merging).
   [APB-V]  "APB-V: ..." machine review (pith.science): "Core claim" and
            "What carries the argument" (top-lp KVs per block ranked by the
            query block's attention scores, all-gathered as passing blocks from
@@ -67,7 +67,8 @@ def split_sequence(la: int, V: int, L: int, n_q: int) -> dict:
 def block_scores(q, k, la, V, L, n_q, scale=None):
     """Query-to-context importance of every key of every block.
 
-    [Spava] Figure 5 caption ("Q_qr K^(h)T estimates KV importance");
+    [Spava] Figure 5 caption (the query block's logits Q_qr K^(h)T rank
+    the keys of block h);
     [APB-V] "What carries the argument" (ranking by query-to-context
     attention scores).  Softmax restricted to block h, summed over query
     tokens and the query heads of the group.
@@ -367,15 +368,16 @@ def approx_prefill(q, k, v, la, V, L, n_q, lp, scale=None, idx=None, with_scores
 
 
 def sampled_rows(q, k, v, kp, vp, la, V, L, n_q, rows, scale=None):
-    """Outputs of chosen (token, head) pairs, computed one by one.
+    """Outputs of chosen (token, head) pairs.
 
     For full-size workloads where the whole oracle is too slow.  Each row is
-    computed from its own key list exactly as in ``approx_prefill``: the key
-    list of a context token of host h is [anchor, passing blocks 0..h-1,
-    own block up to the token] -- the causal part is a prefix of host h's
-    full list, built once per (KV head, host).  Query tokens go through
-    their V+1 partials and the merge.  Inputs are converted to float64 one
-    KV head at a time.
+    computed from its own key list exactly as in ``approx_prefill``: a
+    context token t of host h sees [anchor, passing blocks 0..h-1, own block
+    up to t] -- a prefix of host h's full list, so the chosen rows of one
+    (KV head, host) go through ``attend`` together, each masked to its own
+    prefix; anchor tokens see the anchor up to themselves.  Query tokens go
+    through their V+1 partials and the merge.  Inputs are converted to
+    float64 one KV head at a time.
     Returns O [len(rows), d], LSE [len(rows)].
     """
     Hq, d = q.shape[1], q.shape[2]
@@ -395,22 +397,27 @@ def sampled_rows(q, k, v, kp, vp, la, V, L, n_q, rows, scale=None):
         vg = np.asarray(v[:, g], dtype=np.float64)
         kpg = np.asarray(kp[g], dtype=np.float64).reshape(V * lp, d)
         vpg = np.asarray(vp[g], dtype=np.float64).reshape(V * lp, -1)
-        host_lists = {}
-        for n in sorted(mine, key=lambda n: rows[n][0]):
-            t, a = rows[n]
-            qr = np.asarray(q[t, a], dtype=np.float64)[None, :]
-            if t < la:                                              # anchor token
-                keys, vals = kg[:t + 1], vg[:t + 1]
-            elif t < q0:                                            # context token of host h
-                h = (t - la) // L
+        # Rows that share a key list: the anchor ("a"), host h's context
+        # tokens (h), and each query token on its own.
+        groups = {}
+        for n in mine:
+            t = rows[n][0]
+            key = "a" if t < la else ((t - la) // L if t < q0 else ("q", n))
+            groups.setdefault(key, []).append(n)
+        for key, ns in groups.items():
+            toks = np.array([rows[n][0] for n in ns])
+            qr = np.stack([np.asarray(q[rows[n][0], rows[n][1]], dtype=np.float64) for n in ns])
+            if key == "a":                                          # anchor tokens: causal
+                keys, vals = kg[:la], vg[:la]
+                n_vis = toks + 1
+            elif not isinstance(key, tuple):                        # context tokens of host h
+                h = key
                 b0 = la + h * L
-                if h not in host_lists:
-                    host_lists = {h: (
-                        np.concatenate([kg[:la], kpg[:h * lp], kg[b0:b0 + L]], axis=0),
-                        np.concatenate([vg[:la], vpg[:h * lp], vg[b0:b0 + L]], axis=0))}
-                n_vis = la + h * lp + (t - b0) + 1
-                keys, vals = host_lists[h][0][:n_vis], host_lists[h][1][:n_vis]
+                keys = np.concatenate([kg[:la], kpg[:h * lp], kg[b0:b0 + L]], axis=0)
+                vals = np.concatenate([vg[:la], vpg[:h * lp], vg[b0:b0 + L]], axis=0)
+                n_vis = la + h * lp + (toks - b0) + 1
             else:                                                   # query token: partials + merge
+                t = toks[0]
                 parts_o, parts_l = [], []
                 keys = np.concatenate([kg[:la], kg[q0:t + 1]], axis=0)
                 vals = np.concatenate([vg[:la], vg[q0:t + 1]], axis=0)
@@ -421,10 +428,11 @@ def sampled_rows(q, k, v, kp, vp, la, V, L, n_q, rows, scale=None):
                     oh, lh = attend(qr, kg[b0:b0 + L], vg[b0:b0 + L], np.ones((1, L), bool), scale)
                     parts_o.append(oh[0]); parts_l.append(lh[0])
                 o, lse = lse_merge(np.stack(parts_o)[:, None, :], np.stack(parts_l)[:, None])
-                outO[n], outL[n] = o[0], lse[0]
+                outO[ns[0]], outL[ns[0]] = o[0], lse[0]
                 continue
-            o, lse = attend(qr, keys, vals, np.ones((1, keys.shape[0]), bool), scale)
-            outO[n], outL[n] = o[0], lse[0]
+            vis = np.arange(keys.shape[0])[None, :] < n_vis[:, None]
+            o, lse = attend(qr, keys, vals, vis, scale)
+            outO[ns], outL[ns] = o, lse
     return outO, outL
 
 

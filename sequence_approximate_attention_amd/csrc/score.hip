@@ -1,7 +1,7 @@
 // Block scoring and top-lp selection.
 //
-// Scoring (Figure 5 caption of the Spava page: Q_qr K^(h)T estimates KV
-// importance; "What carries the argument" in the APB-V review: keys ranked by
+// Scoring (Figure 5 caption of the Spava page: the query block's logits
+// against block h rank that block's keys; "What carries the argument" in the APB-V review: keys ranked by
 // query-to-context attention scores).  For block h and KV head g the score of
 // key j is the sum over the query block's rows r = (token i, head a in g) of
 // softmax_j(q_r . k_j * scale) over the block's L keys.  It takes two passes

@@ -331,6 +331,7 @@ def test_sampled_rows_agree_with_full_oracle():
     q, k, v = rand_qkv(rng, N, Hq, Hkv, d)
     r = O.approx_prefill(q, k, v, la, V, L, n_q, lp=3)
     rows = [(t, a) for t in (0, 5, 6, 15, 16, 35, 36, 39) for a in (0, 3)]
+    rows += [(t, a) for t in range(N) for a in range(Hq)]   # every row, grouped per host
     o, l = O.sampled_rows(q, k, v, r["kp"], r["vp"], la, V, L, n_q, rows)
     for n, (t, a) in enumerate(rows):
         np.testing.assert_allclose(o[n], r["O"][t, a], atol=1e-13)
