@@ -114,8 +114,16 @@ __global__ __launch_bounds__(256) void vtranspose_kernel(AttnArgs a, uint16_t* _
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partial attention results (axiom on Eq. 5 / Appendix A
 // in the APB-V review: merging through the FlashAttention lse is exact).
-// One thread per (row, head, 4 channels).
+// One thread per (row, head, 4 channels).  The partials are taken in chunks
+// of at most kMergeChunk: every LSE and O load of a chunk is issued before
+// any of them is used, so a wave has a whole chunk of reads in flight at once
+// (one memory round trip per chunk), and the chunks are merged online: the
+// running maximum m, the weight sum and the weighted O are rescaled when a
+// chunk raises m.  The sums run in partial order, so the result is
+// deterministic.
 // ---------------------------------------------------------------------------
+constexpr int kMergeChunk = 16;
+
 __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
                                                     const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part,
@@ -132,26 +140,40 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
   const float* lp_ra = lse_part + (long)a * R + r;                  // + p * H * R
   const float* op_ra = o_part + ((long)r * H + a) * D + c4 * 4;      // + p * R * H * D
   const long lp_step = (long)H * R, op_step = (long)R * H * D;
-  float m = -INFINITY;
-#pragma unroll 8
-  for (int p = 0; p < P; ++p) m = fmaxf(m, lp_ra[p * lp_step]);
+  // Chunks of equal size (the last one no longer than the others).
+  const int n_chunks = (P + kMergeChunk - 1) / kMergeChunk;
+  const int cs = (P + n_chunks - 1) / n_chunks;
+  float m = -INFINITY, wsum = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.0f;
-  if (m != -INFINITY) {
-    // The partials are read kMergeBatch at a time, all loads first, so each
-    // wave keeps that many reads in flight; the sums still run in p order.
-    constexpr int kMergeBatch = 8;
-    int p = 0;
-    for (; p + kMergeBatch <= P; p += kMergeBatch) {
-      float l[kMergeBatch];
-      float4 x[kMergeBatch];
+  for (int p0 = 0; p0 < P; p0 += cs) {
+    const int n = min(cs, P - p0);
+    float l[kMergeChunk];
+    float4 x[kMergeChunk];
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        l[u] = lp_ra[(p + u) * lp_step];
-        x[u] = *(const float4*)(op_ra + (p + u) * op_step);
+    for (int u = 0; u < kMergeChunk; ++u) {
+      if (u < n) {
+        l[u] = lp_ra[(p0 + u) * lp_step];
+        x[u] = *(const float4*)(op_ra + (p0 + u) * op_step);
       }
+    }
+    float mc = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < kMergeChunk; ++u)
+      if (u < n) mc = fmaxf(mc, l[u]);
+    const float m_new = fmaxf(m, mc);
+    if (m_new == -INFINITY) continue;   // no finite partial yet
+    if (m_new != m) {                   // move the reference (0 * the empty start is 0)
+      const float sc = (m == -INFINITY) ? 0.0f : expf(m - m_new);
+      acc.x *= sc;
+      acc.y *= sc;
+      acc.z *= sc;
+      acc.w *= sc;
+      wsum *= sc;
+      m = m_new;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      if (u < n) {
         const float w = expf(l[u] - m);
         acc.x += w * x[u].x;
         acc.y += w * x[u].y;
@@ -159,15 +181,6 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
         acc.w += w * x[u].w;
         wsum += w;
       }
-    }
-    for (; p < P; ++p) {
-      const float w = expf(lp_ra[p * lp_step] - m);
-      const float4 x = *(const float4*)(op_ra + p * op_step);
-      acc.x += w * x.x;
-      acc.y += w * x.y;
-      acc.z += w * x.z;
-      acc.w += w * x.w;
-      wsum += w;
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
