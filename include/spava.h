@@ -152,6 +152,29 @@ int spava_score_topk(const spava_plan* plan, const void* q, const void* k,
                      void* stream);
 
 /*
+ * Step 1 for callers that cannot allocate (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it): the
+ * same scores and selection as spava_score_topk, bit for bit, with the
+ * workspace taken from a static device array of SPAVA_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of a caller buffer.  Calls no hipMalloc,
+ * hipFree or allocating library routine.
+ *   q, k, scores, idx   as spava_score_topk (scores may be NULL: the scores
+ *                       then live in the static scratch too)
+ * Errors as spava_score_topk; SPAVA_EWORKSPACE when the plan needs more than
+ * SPAVA_NOALLOC_SCRATCH_BYTES (the size spava_score_topk_ws_bytes reports,
+ * less the scores' room when scores is not NULL), checked on the host before
+ * anything is enqueued.  Each GPU holds one copy of the array (64 MiB) from
+ * the first call on it until the process ends.  Every call on one GPU shares
+ * that copy: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  Nothing in the scratch needs
+ * to start at zero (every byte read is written earlier in the same call).
+ */
+#define SPAVA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int spava_score_topk_noalloc(const spava_plan* plan, const void* q,
+                             const void* k, float* scores, int32_t* idx,
+                             void* stream);
+
+/*
  * Workspace bytes spava_score_topk_context needs: as spava_score_topk_ws_bytes
  * with the block's L tokens as the scoring rows, float32 [V][Hkv][L*G] for
  * float32 plans and float32 [V][Hkv][L*G][2] (one key chunk) for bf16 plans;

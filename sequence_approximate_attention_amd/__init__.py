@@ -28,7 +28,9 @@ SPAVA_PHASE_ALL, SPAVA_PHASE_LOCAL, SPAVA_PHASE_PASSING = 0, 1, 2
 EXPORTS = ("spava_version", "spava_last_error", "spava_plan_check", "spava_score_topk_ws_bytes",
            "spava_score_topk", "spava_gather_passing", "spava_attn_fwd_ws_bytes", "spava_attn_fwd",
            "spava_lse_merge", "spava_score_topk_context_ws_bytes", "spava_score_topk_context",
-           "spava_kv_overlap", "spava_attn_fwd_phase", "spava_score_topk_from_partials")
+           "spava_kv_overlap", "spava_attn_fwd_phase", "spava_score_topk_from_partials",
+           "spava_score_topk_noalloc")
+SPAVA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SpavaError(RuntimeError):
@@ -66,6 +68,7 @@ def lib():
         L.spava_score_topk_ws_bytes.argtypes = [P]
         L.spava_score_topk_ws_bytes.restype = sz
         L.spava_score_topk.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_score_topk_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
         L.spava_score_topk_context_ws_bytes.argtypes = [P]
         L.spava_score_topk_context_ws_bytes.restype = sz
         L.spava_score_topk_context.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -188,6 +191,19 @@ def spava_score_topk(plan: Plan, q, k, scores, idx, ws, stream=None):
     _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
     _check(lib().spava_score_topk(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spava_score_topk_noalloc(plan: Plan, q, k, scores, idx, stream=None):
+    """spava_score_topk with the library's static scratch in place of a
+    workspace (no allocation; calls overlapping on one GPU race).  scores may
+    be None."""
+    p = plan
+    _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
+    _expect(k, (p.n_tokens, p.n_kv_heads, p.head_dim), p.torch_dtype, "k", p.kv_strides())
+    _expect(scores, (p.n_hosts, p.n_kv_heads, p.host_len), torch.float32, "scores")
+    _expect(idx, (p.n_hosts, p.n_kv_heads, p.lp), torch.int32, "idx")
+    _check(lib().spava_score_topk_noalloc(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(scores), _ptr(idx),
+                                          _stream(stream)))
 
 
 def spava_score_topk_context(plan: Plan, q, k, scores, idx, ws, stream=None):

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "spava_common.h"
 
 namespace spava {
@@ -22,6 +24,42 @@ int fail(int code, const char* fmt, ...) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Scratch memory of spava_score_topk_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = SPAVA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or NULL (with the
+// error recorded) if it cannot be had.
+void* scratch_on_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(SPAVA_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(SPAVA_EUNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(SPAVA_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 int check_plan(const spava_plan* p) {
   if (!p) return fail(SPAVA_EINVAL, "plan is NULL");
@@ -254,6 +292,26 @@ size_t spava_score_topk_ws_bytes(const spava_plan* plan) {
 int spava_score_topk(const spava_plan* plan, const void* q, const void* k, float* scores,
                      int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   return score_topk("spava_score_topk", false, plan, q, k, scores, idx, ws, ws_bytes, stream);
+}
+
+int spava_score_topk_noalloc(const spava_plan* plan, const void* q, const void* k, float* scores,
+                             int32_t* idx, void* stream) {
+  const char* name = "spava_score_topk_noalloc";
+  int rc = check_plan(plan);
+  if (rc) return rc;
+  // The same checks as spava_score_topk, then the size, all before the
+  // device is touched.
+  if (!q || !k || (plan->lp > 0 && !idx))
+    return fail(SPAVA_EINVAL, "%s: q, k (and idx when lp > 0) must be non-NULL", name);
+  if (!aligned16(q) || !aligned16(k) || (scores && !aligned16(scores)) || (idx && !aligned16(idx)))
+    return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
+  const size_t need = stats_bytes(plan, false) + (scores ? 0 : scores_bytes(plan));
+  if (need > kScratchBytes)
+    return fail(SPAVA_EWORKSPACE, "%s: this plan needs %zu bytes of scratch; the static scratch holds %zu "
+                "(pass scores, or use spava_score_topk with a workspace)", name, need, kScratchBytes);
+  void* ws = scratch_on_current_device();
+  if (!ws) return SPAVA_ELAUNCH;
+  return score_topk(name, false, plan, q, k, scores, idx, ws, kScratchBytes, stream);
 }
 
 size_t spava_score_topk_context_ws_bytes(const spava_plan* plan) {

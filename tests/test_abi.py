@@ -168,3 +168,20 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     # Scores from the query partials: lse_part is required when n_query > 0.
     assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, fake, None, fake, fake, None) == S.SPAVA_EINVAL
     assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, odd, fake, fake, fake, None) == S.SPAVA_EINVAL
+
+
+def test_noalloc_scoring_rejects_plans_beyond_its_scratch_on_the_host():
+    # The 256K frame-shaped layer fits the static scratch even with the
+    # scores kept there; twice its query rows do not.  The rejection happens
+    # before the device is touched, so this runs without a GPU.
+    fits = S.Plan(4096, 32, 8128, 512, 28, 4, 128, 4096)
+    assert S.spava_score_topk_ws_bytes(fits) <= S.SPAVA_NOALLOC_SCRATCH_BYTES
+    big = S.Plan(4096, 32, 8128, 1024, 28, 4, 128, 4096)
+    assert S.spava_score_topk_ws_bytes(big) > S.SPAVA_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: the call fails validation first
+    rc = S.lib().spava_score_topk_noalloc(ctypes.byref(big.c()), fake, fake, fake, fake, None)
+    assert rc == S.SPAVA_EWORKSPACE
+    assert b"static scratch" in S.lib().spava_last_error()
+    # Argument checks as spava_score_topk: NULL idx with lp > 0.
+    rc = S.lib().spava_score_topk_noalloc(ctypes.byref(fits.c()), fake, fake, fake, None, None)
+    assert rc == S.SPAVA_EINVAL
