@@ -204,6 +204,21 @@ def cpu_baseline(w, x, selector="query", attn_budget_s=10.0, row_stride=61):
     }
 
 
+# Row-statistics work (scoring rows x keys, summed over blocks and KV heads)
+# above which the Figure 5 order pays for its second attention launch: the
+# pass it saves then outweighs the first launch's tail.  Measured: 256K
+# frame shape (3.7e9) and 128K text layer (2.1e9) faster with partials-first,
+# the 32K layers (6.3e7) faster in one pass.
+PARTIALS_FIRST_MIN_WORK = 1e9
+
+
+def pick_order(w, selector="query"):
+    if selector != "query" or w.n_query == 0 or w.n_hosts < 2:
+        return "one-pass"
+    work = w.n_query * w.group * w.host_len * w.n_hosts * w.n_kv_heads
+    return "partials-first" if work >= PARTIALS_FIRST_MIN_WORK else "one-pass"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,10 +230,12 @@ def main():
     ap.add_argument("--dense", action="store_true",
                     help="time the library's dense causal plan over the workload's tokens and heads "
                          "(one host of N tokens, no anchor, query or passing blocks) instead")
-    ap.add_argument("--order", choices=("one-pass", "partials-first"), default="one-pass",
+    ap.add_argument("--order", choices=("auto", "one-pass", "partials-first"), default="auto",
                     help="one-pass: score, gather, one attention call; partials-first: the rows "
                          "that need no passing block first, scores from the query partials' LSEs, "
-                         "then gather and the remaining rows (Figure 5 ordering)")
+                         "then gather and the remaining rows (Figure 5 ordering); auto: "
+                         "partials-first when the separate row-statistics pass it saves is long "
+                         "(see pick_order)")
     ap.add_argument("--selector", choices=("query", "context"), default="query",
                     help="which rule scores the keys: the query block's attention (the pages' "
                          "method) or each block's own tokens (the referee's alternative)")
@@ -266,6 +283,8 @@ def main():
     stream = torch.cuda.current_stream()
     q0 = wl.n_anchor + wl.n_hosts * wl.host_len
 
+    if args.order == "auto":
+        args.order = pick_order(wl, args.selector)
     if args.order == "partials-first" and args.selector == "context":
         print("--order partials-first scores from the query partials; it takes the query selector",
               file=sys.stderr)
@@ -338,7 +357,7 @@ def main():
     # library (one host of N tokens), the one-GPU analogue of the pages'
     # speedups over FlashAttention.
     dense_ms = None
-    if not args.dense and not args.no_dense_context and args.order == "one-pass":
+    if not args.dense and not args.no_dense_context:
         dplan = S.Plan(0, 1, wl.n_tokens, 0, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 0, plan.dtype)
         db = S.alloc_buffers(dplan, dev)
         d_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
