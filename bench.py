@@ -290,7 +290,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     attn = lambda phase: S.spava_attn_fwd_phase(plan, phase, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse,
-                                                bufs.o_part, bufs.lse_part, bufs.ws_attn, stream)
+                                                bufs.o_part, bufs.lse_part, stream)
     rec = lambda ev, i: ev[i].record(stream) if ev is not None else None
 
     def step(ev=None):
@@ -364,7 +364,7 @@ def main():
         dts = []
         for i in range(6):
             d_ev[0].record(stream)
-            S.spava_attn_fwd(dplan, q, k, v, db.kp, db.vp, db.o, db.lse, db.o_part, db.lse_part, db.ws_attn, stream)
+            S.spava_attn_fwd(dplan, q, k, v, db.kp, db.vp, db.o, db.lse, db.o_part, db.lse_part, stream)
             d_ev[1].record(stream)
             torch.cuda.synchronize()
             if i >= 2:

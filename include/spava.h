@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SPAVA_VERSION 100
+#define SPAVA_VERSION 200
 
 #define SPAVA_OK 0
 #define SPAVA_EINVAL 1        /* null pointer, bad size, misaligned pointer   */
@@ -84,7 +84,9 @@ extern "C" {
  *                  (Hq*d, d and Hkv*d, d), so a zero-initialised plan tail
  *                  keeps the dense tensors below.  Each stride must be a
  *                  multiple of 16 bytes / element size (rows stay 16-byte
- *                  aligned); a packed QKV projection output [N][Hq+2Hkv][d]
+ *                  aligned), and each token stride at least d (a token's
+ *                  channels end before the next token's start) and below
+ *                  2^24 bytes; a packed QKV projection output [N][Hq+2Hkv][d]
  *                  is q = qkv, k = qkv + Hq*d, v = qkv + (Hq+Hkv)*d with
  *                  token strides (Hq+2Hkv)*d and head strides d.
  * N = la + V*L + n_q rows in total; N * max(Hq, Hkv) * d must be < 2^31, and
@@ -233,12 +235,6 @@ int spava_gather_passing(const spava_plan* plan, const void* k, const void* v,
                          const int32_t* idx, void* kp, void* vp, void* stream);
 
 /*
- * Workspace bytes spava_attn_fwd needs: key-contiguous copies of V and of the
- * passing values, padded per segment to the kernel's key tile.
- */
-size_t spava_attn_fwd_ws_bytes(const spava_plan* plan);
-
-/*
  * Step 3: fused approximate attention forward (Figure 3 caption; review
  * "Core claim"; Referee Report, Eq. (4) key list [K_a, K_p, K^(h)]).
  *   anchor token t < la:           keys 0..t                       (causal)
@@ -253,14 +249,13 @@ size_t spava_attn_fwd_ws_bytes(const spava_plan* plan);
  *   lse       [Hq][N]             float32; columns [0, la+V*L) written
  *   o_part    [V+1][n_q][Hq][d]   float32, written (may be NULL if n_q == 0)
  *   lse_part  [V+1][Hq][n_q]      float32, written (may be NULL if n_q == 0)
- *   ws        >= spava_attn_fwd_ws_bytes(plan) bytes of scratch
+ * No workspace: K and V tiles are read straight from k, v, kp, vp.
  * Dense causal attention is the plan {la=0, V=1, L=N, n_q=0, lp=0}
  * (one host degrades to standard attention).
  */
 int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k,
                    const void* v, const void* kp, const void* vp, void* o,
-                   float* lse, float* o_part, float* lse_part, void* ws,
-                   size_t ws_bytes, void* stream);
+                   float* lse, float* o_part, float* lse_part, void* stream);
 
 /*
  * Step 3 in two phases, for the ordering of the Spava page's Figure 5 (the
@@ -270,11 +265,9 @@ int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k,
  * spava_attn_fwd call writes, bit for bit.
  *   SPAVA_PHASE_LOCAL    anchor rows, context rows of host 0 and the query
  *                        partials o_part/lse_part (no passing block is read:
- *                        kp, vp may be NULL); fills the V^T copy of ws.
+ *                        kp, vp may be NULL).
  *   SPAVA_PHASE_PASSING  context rows of hosts 1..V-1 (o_part, lse_part are
- *                        not touched and may be NULL); ws must be the
- *                        workspace the LOCAL phase of the same plan and v
- *                        filled, unchanged since.
+ *                        not touched and may be NULL).
  *   SPAVA_PHASE_ALL      the same as spava_attn_fwd.
  * The order of calls is then: spava_attn_fwd_phase(LOCAL) ->
  * spava_score_topk_from_partials -> spava_gather_passing ->
@@ -283,8 +276,7 @@ int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k,
 int spava_attn_fwd_phase(const spava_plan* plan, int32_t phase, const void* q,
                          const void* k, const void* v, const void* kp,
                          const void* vp, void* o, float* lse, float* o_part,
-                         float* lse_part, void* ws, size_t ws_bytes,
-                         void* stream);
+                         float* lse_part, void* stream);
 
 /*
  * Step 1 after spava_attn_fwd_phase(LOCAL): the same scores and selection as

@@ -26,7 +26,7 @@ SPAVA_OK, SPAVA_EINVAL, SPAVA_EUNSUPPORTED, SPAVA_EWORKSPACE, SPAVA_ELAUNCH = ra
 SPAVA_BF16, SPAVA_F32 = 0, 1
 SPAVA_PHASE_ALL, SPAVA_PHASE_LOCAL, SPAVA_PHASE_PASSING = 0, 1, 2
 EXPORTS = ("spava_version", "spava_last_error", "spava_plan_check", "spava_score_topk_ws_bytes",
-           "spava_score_topk", "spava_gather_passing", "spava_attn_fwd_ws_bytes", "spava_attn_fwd",
+           "spava_score_topk", "spava_gather_passing", "spava_attn_fwd",
            "spava_lse_merge", "spava_score_topk_context_ws_bytes", "spava_score_topk_context",
            "spava_kv_overlap", "spava_attn_fwd_phase", "spava_score_topk_from_partials",
            "spava_score_topk_noalloc")
@@ -73,12 +73,10 @@ def lib():
         L.spava_score_topk_context_ws_bytes.restype = sz
         L.spava_score_topk_context.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.spava_kv_overlap.argtypes = [i32, i32, vp, vp, vp, vp]
-        L.spava_attn_fwd_phase.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_attn_fwd_phase.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.spava_score_topk_from_partials.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.spava_gather_passing.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        L.spava_attn_fwd_ws_bytes.argtypes = [P]
-        L.spava_attn_fwd_ws_bytes.restype = sz
-        L.spava_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.spava_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.spava_lse_merge.argtypes = [i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, i32, vp]
         _lib = L
     return _lib
@@ -179,10 +177,6 @@ def spava_score_topk_context_ws_bytes(plan: Plan) -> int:
     return lib().spava_score_topk_context_ws_bytes(ctypes.byref(plan.c()))
 
 
-def spava_attn_fwd_ws_bytes(plan: Plan) -> int:
-    return lib().spava_attn_fwd_ws_bytes(ctypes.byref(plan.c()))
-
-
 def spava_score_topk(plan: Plan, q, k, scores, idx, ws, stream=None):
     p = plan
     _expect(q, (p.n_tokens, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
@@ -242,14 +236,14 @@ def spava_gather_passing(plan: Plan, k, v, idx, kp, vp, stream=None):
                                       _ptr(vp), _stream(stream)))
 
 
-def spava_attn_fwd(plan: Plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream=None):
-    spava_attn_fwd_phase(plan, SPAVA_PHASE_ALL, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream)
+def spava_attn_fwd(plan: Plan, q, k, v, kp, vp, o, lse, o_part, lse_part, stream=None):
+    spava_attn_fwd_phase(plan, SPAVA_PHASE_ALL, q, k, v, kp, vp, o, lse, o_part, lse_part, stream)
 
 
-def spava_attn_fwd_phase(plan: Plan, phase: int, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, stream=None):
+def spava_attn_fwd_phase(plan: Plan, phase: int, q, k, v, kp, vp, o, lse, o_part, lse_part, stream=None):
     """SPAVA_PHASE_LOCAL: anchor rows, host 0's context rows and the query
-    partials; SPAVA_PHASE_PASSING: context rows of hosts 1..V-1 (after the
-    LOCAL phase, with its workspace); SPAVA_PHASE_ALL: everything."""
+    partials; SPAVA_PHASE_PASSING: context rows of hosts 1..V-1;
+    SPAVA_PHASE_ALL: everything."""
     p = plan
     N = p.n_tokens
     _expect(q, (N, p.n_q_heads, p.head_dim), p.torch_dtype, "q", p.q_strides())
@@ -262,8 +256,7 @@ def spava_attn_fwd_phase(plan: Plan, phase: int, q, k, v, kp, vp, o, lse, o_part
     _expect(o_part, (p.n_hosts + 1, p.n_query, p.n_q_heads, p.head_dim), torch.float32, "o_part")
     _expect(lse_part, (p.n_hosts + 1, p.n_q_heads, p.n_query), torch.float32, "lse_part")
     _check(lib().spava_attn_fwd_phase(ctypes.byref(p.c()), phase, _ptr(q), _ptr(k), _ptr(v), _ptr(kp),
-                                      _ptr(vp), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(stream)))
+                                      _ptr(vp), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
 def spava_score_topk_from_partials(plan: Plan, q, k, lse_part, scores, idx, stream=None):
@@ -307,7 +300,6 @@ class Buffers:
     o_part: torch.Tensor
     lse_part: torch.Tensor
     ws_score: torch.Tensor
-    ws_attn: torch.Tensor
 
 
 def alloc_buffers(plan: Plan, device="cuda") -> Buffers:
@@ -325,7 +317,6 @@ def alloc_buffers(plan: Plan, device="cuda") -> Buffers:
         o_part=torch.empty((p.n_hosts + 1, p.n_query, p.n_q_heads, p.head_dim), dtype=f32, device=device),
         lse_part=torch.empty((p.n_hosts + 1, p.n_q_heads, p.n_query), dtype=f32, device=device),
         ws_score=torch.empty(max(256, spava_score_topk_ws_bytes(p)), dtype=torch.uint8, device=device),
-        ws_attn=torch.empty(max(256, spava_attn_fwd_ws_bytes(p)), dtype=torch.uint8, device=device),
     )
 
 
@@ -343,7 +334,7 @@ def prefill(plan: Plan, q, k, v, bufs: Buffers | None = None, idx=None, stream=N
     if bufs is None:
         bufs = alloc_buffers(p, q.device)
     attn = lambda phase: spava_attn_fwd_phase(p, phase, q, k, v, bufs.kp, bufs.vp, bufs.o, bufs.lse,
-                                              bufs.o_part, bufs.lse_part, bufs.ws_attn, stream)
+                                              bufs.o_part, bufs.lse_part, stream)
     if partials_first:
         attn(SPAVA_PHASE_LOCAL)
         if idx is None:

@@ -91,6 +91,13 @@ int check_plan(const spava_plan* p) {
   const double q_sh = p->q_stride_head ? (double)p->q_stride_head : (double)p->head_dim;
   const double kv_st = p->kv_stride_tok ? (double)p->kv_stride_tok : (double)p->n_kv_heads * p->head_dim;
   const double kv_sh = p->kv_stride_head ? (double)p->kv_stride_head : (double)p->head_dim;
+  // A token's d channels end before the next token starts (copies of a run
+  // end at its last row's d channels), and a token stride stays below 2^24
+  // bytes (tile-row offsets are 24-bit products).
+  if (q_st < p->head_dim || kv_st < p->head_dim)
+    return fail(SPAVA_EINVAL, "token strides must be at least head_dim (%d) elements", p->head_dim);
+  if (q_st * esz >= 16777216.0 || kv_st * esz >= 16777216.0)
+    return fail(SPAVA_EINVAL, "token strides must stay below 2^24 bytes");
   if ((N - 1) * q_st + (p->n_q_heads - 1) * q_sh + p->head_dim >= 2147483648.0 ||
       (N - 1) * kv_st + (p->n_kv_heads - 1) * kv_sh + p->head_dim >= 2147483648.0)
     return fail(SPAVA_EINVAL, "q or k/v extends over 2^31 elements under its strides");
@@ -125,7 +132,6 @@ AttnArgs make_args(const spava_plan* p) {
   a.kv_sh = p->kv_stride_head ? p->kv_stride_head : a.D;
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)a.D);
   a.scale_log2 = a.scale * 1.44269504088896340736f;
-  a.vl = VtLayout::make(a.la, a.V, a.L, a.nq, a.lp);
   a.f32 = p->dtype == SPAVA_F32;
   const int bm = a.f32 ? kRowsPerUnitF32 : attn_bf16_rows_per_unit();
   a.rows_per_unit = bm;
@@ -174,30 +180,18 @@ int launched(hipError_t e, const char* what) {
   return SPAVA_OK;
 }
 
-size_t vt_bytes(const spava_plan* p, size_t* off_pass) {
-  const VtLayout vl = VtLayout::make(p->n_anchor, p->n_hosts, p->host_len, p->n_query, p->lp);
-  const size_t main = (size_t)p->n_kv_heads * p->head_dim * vl.main_len * 2;
-  const size_t pass = (size_t)p->n_kv_heads * p->head_dim * vl.pass_len * 2;
-  const size_t main_al = (main + 255) / 256 * 256;
-  if (off_pass) *off_pass = main_al;
-  return main_al + (pass + 255) / 256 * 256;
-}
-
 // Argument checks and launches of the attention, all units or one phase.
 int attn_fwd(const char* name, int phase, const spava_plan* plan, const void* q, const void* k, const void* v,
-             const void* kp, const void* vp, void* o, float* lse, float* o_part, float* lse_part, void* ws,
-             size_t ws_bytes, void* stream) {
+             const void* kp, const void* vp, void* o, float* lse, float* o_part, float* lse_part, void* stream) {
   int rc = check_plan(plan);
   if (rc) return rc;
   const bool need_pass = phase != kPhaseLocal && plan->lp > 0 && plan->n_hosts > 1;
   const bool need_part = phase != kPhasePassing && plan->n_query > 0;
-  if (!q || !k || !v || !o || !lse || !ws || (need_pass && (!kp || !vp)) || (need_part && (!o_part || !lse_part)))
+  if (!q || !k || !v || !o || !lse || (need_pass && (!kp || !vp)) || (need_part && (!o_part || !lse_part)))
     return fail(SPAVA_EINVAL, "%s: NULL pointer", name);
-  const void* ptrs[] = {q, k, v, kp, vp, o, lse, o_part, lse_part, ws};
+  const void* ptrs[] = {q, k, v, kp, vp, o, lse, o_part, lse_part};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SPAVA_EINVAL, "%s: pointers must be 16-byte aligned", name);
-  const size_t need = plan->dtype == SPAVA_F32 ? 256 : vt_bytes(plan, nullptr);
-  if (ws_bytes < need) return fail(SPAVA_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   AttnArgs a = make_args(plan);
   if (phase != kPhaseAll) a.n_ctx_first = a.V;   // phases split the order after host 1
@@ -216,14 +210,6 @@ int attn_fwd(const char* name, int phase, const spava_plan* plan, const void* q,
     e = launch_attn_f32(a, s);
     return launched(e, "attention (float32)");
   }
-  size_t off_pass = 0;
-  vt_bytes(plan, &off_pass);
-  uint16_t* vt = (uint16_t*)ws;
-  uint16_t* vpt = (uint16_t*)((char*)ws + off_pass);
-  e = launch_vtranspose(a, vt, vpt, phase, s);
-  if (e != hipSuccess) return launched(e, "V transpose");
-  a.vt = vt;
-  a.vpt = vpt;
   e = launch_attn_bf16(a, s);
   return launched(e, "attention (bf16)");
 }
@@ -360,26 +346,18 @@ int spava_gather_passing(const spava_plan* plan, const void* k, const void* v, c
   return launched(e, "gather");
 }
 
-size_t spava_attn_fwd_ws_bytes(const spava_plan* plan) {
-  if (check_plan(plan) != SPAVA_OK) return 0;
-  if (plan->dtype == SPAVA_F32) return 256;
-  return vt_bytes(plan, nullptr);
-}
-
 int spava_attn_fwd(const spava_plan* plan, const void* q, const void* k, const void* v,
                    const void* kp, const void* vp, void* o, float* lse, float* o_part,
-                   float* lse_part, void* ws, size_t ws_bytes, void* stream) {
-  return attn_fwd("spava_attn_fwd", kPhaseAll, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, ws_bytes,
-                  stream);
+                   float* lse_part, void* stream) {
+  return attn_fwd("spava_attn_fwd", kPhaseAll, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, stream);
 }
 
 int spava_attn_fwd_phase(const spava_plan* plan, int32_t phase, const void* q, const void* k, const void* v,
                          const void* kp, const void* vp, void* o, float* lse, float* o_part,
-                         float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+                         float* lse_part, void* stream) {
   if (phase != SPAVA_PHASE_ALL && phase != SPAVA_PHASE_LOCAL && phase != SPAVA_PHASE_PASSING)
     return fail(SPAVA_EINVAL, "spava_attn_fwd_phase: phase %d is not SPAVA_PHASE_ALL, _LOCAL or _PASSING", phase);
-  return attn_fwd("spava_attn_fwd_phase", phase, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, ws, ws_bytes,
-                  stream);
+  return attn_fwd("spava_attn_fwd_phase", phase, plan, q, k, v, kp, vp, o, lse, o_part, lse_part, stream);
 }
 
 int spava_score_topk_from_partials(const spava_plan* plan, const void* q, const void* k, const float* lse_part,

@@ -8,22 +8,29 @@
 //   output wave (wave 4+s):  O += V P on the matrix cores, and the tile copies.
 // The softmax wave's vector work then issues while the output wave's MFMAs
 // occupy the matrix core (a single wave can only slip a few vector
-// instructions under its own MFMAs), and every K or V^T fragment read from
+// instructions under its own MFMAs), and every K or V fragment read from
 // LDS still feeds two MFMAs (64 rows per wave).
 //
 // Iteration i (one workgroup barrier each):
 //   softmax wave:  S(i) = K(i) Q^T || P(i-1) = exp2(S(i-1) - m), written to
 //                  LDS with its rescale factor; row maxima of S(i)
 //   output wave:   copies of V(i-1) and K(i+2); O = O*alpha(i-2) + V(i-2) P(i-2)
-// LDS: a 3-slot K ring, a 2-slot V^T ring (filled by buffer_load_dwordx4 ...
-// lds straight from memory) and a double-buffered P exchange.
+// LDS: a 2-slot V ring at address 0 (so every V read is a lane offset plus an
+// immediate), a 3-slot K ring (both filled by buffer_load_dwordx4 ... lds
+// straight from memory) and a double-buffered P exchange.
 //   K tile   [64 keys][D]   row-major, read as the MFMA A operand of S^T
-//   V^T tile [D][64 keys]   key-contiguous, read as the MFMA A operand of O^T
+//   V tile   [64 keys][D]   row-major; gfx950's transposing LDS reads
+//                           (ds_read_b64_tr_b16) give the MFMA A operand of
+//                           O^T = V^T P^T, 8 consecutive keys of one channel
+//                           per lane, with no transposed copy of V anywhere
 //   P tile   [2][4][64 lanes][8 bf16]  already in the B-operand layout
-// K and V^T rows are XOR-swizzled in 16-byte slots (the 16 rows of one
-// ds_read_b128 phase land in distinct banks).  Every copy addresses memory
+// K and V rows are XOR-swizzled in 16-byte slots, each with the swizzle that
+// keeps its reads free of bank conflicts (K: the 16 rows of one ds_read_b128
+// phase; V: the 8 rows x 4 chunks of one transposing read).  Every copy
+// addresses memory
 // inside its tensor: tiles past the end of the walk re-read a tile already
-// visited, K rows past a run's end read its last row, and both are masked.
+// visited, K and V rows past a run's end read its last row, and both are
+// masked (their probabilities are 0).
 //
 // Math: S^T = K Q^T puts one query column per lane, so a row's softmax
 // statistics live in one lane pair (l, l^32) of the softmax wave.  K-tile rows
@@ -48,7 +55,7 @@ constexpr int kBM = kPairs * kWaveRows;     // rows per workgroup (unit)
 constexpr int kBN = kKeyTile;               // keys per tile
 constexpr int kThreads = kWaves * 64;
 constexpr int kKSlots = 3;                  // K ring: K(t) in slot t % 3
-constexpr int kVSlots = 2;                  // V^T ring: V(t) in slot t % 2
+constexpr int kVSlots = 2;                  // V ring: V(t) in slot t % 2
 constexpr int kPBytes = 2 * 4 * 64 * 16;    // P tile of one pair (64 rows x 64 keys, bf16)
 constexpr float kGrowLog2 = 8.0f;
 
@@ -56,20 +63,17 @@ template <int D>
 struct Geo {
   static constexpr int NC = D / 16;                   // 16-wide d chunks (K steps of S)
   static constexpr int NDB = D / 32;                  // 32-row d blocks of O^T
-  static constexpr int KRB = D * 2;                   // bytes per K row
-  static constexpr int KBYTES = kBN * KRB;            // K tile
-  static constexpr int VBYTES = D * kBN * 2;          // V^T tile (rows of 64 keys = 128 B)
-  static constexpr int KINST = KBYTES / 1024 / kPairs;   // copy instructions per output wave
-  static constexpr int VINST = VBYTES / 1024 / kPairs;
+  static constexpr int KRB = D * 2;                   // bytes per K or V row
+  static constexpr int KBYTES = kBN * KRB;            // K tile; a V tile is the same
+  static constexpr int KINST = KBYTES / 1024 / kPairs;   // copy instructions per output wave and tile
 };
 
 // The unit's key runs as scalar fields (selected by value, never by a
 // dynamic index, so that they stay in scalar registers).
 struct SegRun {
   const uint16_t* k;   // key 0 of the run (K or passing K rows)
-  const uint16_t* vt;  // key 0 in the V^T row of channel 0
+  const uint16_t* v;   // its V row (V and K share their layout and strides)
   int kstride;         // elements between consecutive keys
-  int vrow;            // elements between consecutive V^T channel rows
   int len;             // keys
   int causal;          // 1: key token tok0 + j must be <= the query token
   int tok0;
@@ -79,9 +83,8 @@ struct SegRun {
 __device__ __forceinline__ SegRun empty_run() {
   SegRun r;
   r.k = nullptr;
-  r.vt = nullptr;
+  r.v = nullptr;
   r.kstride = 0;
-  r.vrow = 0;
   r.len = 0;
   r.causal = 0;
   r.tok0 = 0;
@@ -89,15 +92,13 @@ __device__ __forceinline__ SegRun empty_run() {
   return r;
 }
 
-// A run of consecutive tokens of K/V head g: tokens [tok0, tok0+len), whose
-// V^T copy starts at key offset vkey of the main V^T row.
-__device__ __forceinline__ SegRun main_run(const AttnArgs& a, int g, int tok0, int len, int vkey,
-                                           int causal) {
+// A run of consecutive tokens of K/V head g: tokens [tok0, tok0+len).
+__device__ __forceinline__ SegRun main_run(const AttnArgs& a, int g, int tok0, int len, int causal) {
   SegRun r;
-  r.k = (const uint16_t*)a.k + (long)tok0 * a.kv_st + (long)g * a.kv_sh;
-  r.vt = a.vt + (long)g * a.D * a.vl.main_len + vkey;
+  const long off = (long)tok0 * a.kv_st + (long)g * a.kv_sh;
+  r.k = (const uint16_t*)a.k + off;
+  r.v = (const uint16_t*)a.v + off;
   r.kstride = (int)a.kv_st;
-  r.vrow = a.vl.main_len;
   r.len = len;
   r.causal = causal;
   r.tok0 = tok0;
@@ -118,25 +119,25 @@ __device__ __forceinline__ void unit_runs(const AttnArgs& a, const Unit& u, SegR
   r2 = empty_run();
   switch (u.kind) {
     case kAnchor:
-      r0 = main_run(a, g, 0, a.la, 0, 1);
+      r0 = main_run(a, g, 0, a.la, 1);
       break;
     case kContext:
-      r0 = main_run(a, g, 0, a.la, 0, 0);
+      r0 = main_run(a, g, 0, a.la, 0);
       if (u.host > 0 && a.lp > 0) {
-        r1.k = (const uint16_t*)a.kp + (long)g * a.V * a.lp * a.D;
-        r1.vt = a.vpt + (long)g * a.D * a.vl.pass_len;
+        const long off = (long)g * a.V * a.lp * a.D;
+        r1.k = (const uint16_t*)a.kp + off;
+        r1.v = (const uint16_t*)a.vp + off;
         r1.kstride = a.D;
-        r1.vrow = a.vl.pass_len;
         r1.len = u.host * a.lp;
       }
-      r2 = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 1);
+      r2 = main_run(a, g, a.la + u.host * a.L, a.L, 1);
       break;
     case kQueryHead:
-      r0 = main_run(a, g, 0, a.la, 0, 0);
-      r1 = main_run(a, g, a.la + a.V * a.L, a.nq, a.vl.off_query, 1);
+      r0 = main_run(a, g, 0, a.la, 0);
+      r1 = main_run(a, g, a.la + a.V * a.L, a.nq, 1);
       break;
     default:  // kQueryBlock
-      r0 = main_run(a, g, a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
+      r0 = main_run(a, g, a.la + u.host * a.L, a.L, 0);
       break;
   }
 }
@@ -150,9 +151,8 @@ __device__ __forceinline__ T pick3(T x0, T x1, T x2, int i) {
 __device__ __forceinline__ SegRun sel(SegRun a0, SegRun a1, SegRun a2, int i) {
   SegRun r;
   r.k = pick3(a0.k, a1.k, a2.k, i);
-  r.vt = pick3(a0.vt, a1.vt, a2.vt, i);
+  r.v = pick3(a0.v, a1.v, a2.v, i);
   r.kstride = pick3(a0.kstride, a1.kstride, a2.kstride, i);
-  r.vrow = pick3(a0.vrow, a1.vrow, a2.vrow, i);
   r.len = pick3(a0.len, a1.len, a2.len, i);
   r.causal = pick3(a0.causal, a1.causal, a2.causal, i);
   r.tok0 = pick3(a0.tok0, a1.tok0, a2.tok0, i);
@@ -190,9 +190,8 @@ __device__ __forceinline__ TileRef tile_ref(const Runs& R, int i) {
   TileRef r;
   r.run = sel(R.r0, R.r1, R.r2, s);
   r.run.k = uni(r.run.k);
-  r.run.vt = uni(r.run.vt);
+  r.run.v = uni(r.run.v);
   r.run.kstride = uni(r.run.kstride);
-  r.run.vrow = uni(r.run.vrow);
   r.run.len = uni(live ? r.run.len : 0);
   r.run.causal = uni(live ? r.run.causal : 0);
   r.run.tok0 = uni(r.run.tok0);
@@ -200,15 +199,14 @@ __device__ __forceinline__ TileRef tile_ref(const Runs& R, int i) {
   return r;
 }
 
-// Per-lane parts of the copy addresses.  A copy instruction moves 1 KB: R
-// rows of the tile (R = 4 for 256-byte K rows, 8 for 128-byte K rows and for
-// V^T rows), lane l writing 16 bytes at LDS slot l % (16 / (R / 4)) of row
-// l / (64 / R).  The XOR swizzle of that row splits into a lane part and a
-// part set by the copy index j: the source chunk is lane_chunk ^ (4 * j')
+// Per-lane parts of the copy addresses (K and V tiles alike).  A copy
+// instruction moves 1 KB: R rows of the tile (R = 4 for 256-byte rows, 8 for
+// 128-byte rows), lane l writing 16 bytes at LDS slot l % (16 / (R / 4)) of
+// row l / (64 / R).  The XOR swizzle of that row splits into a lane part and
+// a part set by the copy index j: the source chunk is lane_chunk ^ (4 * j')
 // with j' = j for 4-row copies and j & 1 for 8-row copies.
 struct LaneCopy {
-  int kq, kx16;   // K: row within the copy, lane chunk * 16
-  int vq, vx16;   // V^T: the same
+  int kq, kx16;   // row within the copy, lane chunk * 16
 };
 template <int D>
 __device__ __forceinline__ LaneCopy lane_copy(int lane) {
@@ -220,8 +218,6 @@ __device__ __forceinline__ LaneCopy lane_copy(int lane) {
     c.kq = lane >> 3;
     c.kx16 = ((lane & 7) ^ (lane >> 4)) << 4;
   }
-  c.vq = lane >> 3;
-  c.vx16 = ((lane & 7) ^ (lane >> 4)) << 4;
   return c;
 }
 
@@ -232,12 +228,12 @@ __device__ __forceinline__ LaneCopy lane_copy(int lane) {
 // (their logits are masked), and past the walk the cursor keeps pointing at a
 // tile it has already visited (or the unit's first run).
 struct Cursor {
-  unsigned long long addr;  // K: first key row of the tile; V^T: its first key in channel row 0
+  unsigned long long addr;  // first key row of the tile (K or V)
   int rem;                  // bytes the copy may read from addr (0: nothing)
-  int stride2;              // bytes between the rows a copy reads (K: keys; V^T: channels)
+  int stride2;              // bytes between keys (below 2^24: a row offset is one 24-bit multiply)
   int left;                 // tiles left in the current run, this one included
   int s;                    // current run; 3 = past the walk
-  int rows;                 // K: rows of the run from this tile on (0 past the walk)
+  int rows;                 // rows of the run from this tile on (0 past the walk)
 };
 
 // Enter run s (or the first later run that has tiles) at its first tile.
@@ -253,24 +249,18 @@ __device__ __forceinline__ void cursor_enter(Cursor& c, const Runs& R, int s) {
   }
   const SegRun r = sel(R.r0, R.r1, R.r2, s);
   c.left = uni(r.nt);
-  if (IS_K) {
-    c.addr = (unsigned long long)uni(r.k);
-    c.stride2 = uni(r.kstride) * 2;
-    c.rows = uni(r.len);
-    c.rem = c.rows * c.stride2;
-  } else {
-    c.addr = (unsigned long long)uni(r.vt);
-    c.stride2 = uni(r.vrow) * 2;
-    c.rem = (D - 1) * c.stride2 + kBN * 2;   // one zero-padded tile
-  }
+  c.addr = (unsigned long long)uni(IS_K ? r.k : r.v);
+  c.stride2 = uni(r.kstride) * 2;
+  c.rows = uni(r.len);
+  c.rem = c.rows * c.stride2;
 }
 
 // Start a cursor at the unit's first run (the address stays valid even when
 // the walk is empty).
 template <int D, bool IS_K>
 __device__ __forceinline__ void cursor_start(Cursor& c, const Runs& R) {
-  c.addr = (unsigned long long)(IS_K ? uni(R.r0.k) : uni(R.r0.vt));
-  c.stride2 = IS_K ? uni(R.r0.kstride) * 2 : uni(R.r0.vrow) * 2;
+  c.addr = (unsigned long long)(IS_K ? uni(R.r0.k) : uni(R.r0.v));
+  c.stride2 = uni(R.r0.kstride) * 2;
   cursor_enter<D, IS_K>(c, R, 0);
 }
 
@@ -278,13 +268,9 @@ template <int D, bool IS_K>
 __device__ __forceinline__ void cursor_next(Cursor& c, const Runs& R) {
   if (c.left > 1) {
     --c.left;
-    if (IS_K) {
-      c.addr += (unsigned long long)(kBN * c.stride2);
-      c.rem -= kBN * c.stride2;
-      c.rows -= kBN;
-    } else {
-      c.addr += kBN * 2;
-    }
+    c.addr += (unsigned long long)(kBN * c.stride2);
+    c.rem -= kBN * c.stride2;
+    c.rows -= kBN;
   } else {
     cursor_enter<D, IS_K>(c, R, c.s + 1);
   }
@@ -299,8 +285,8 @@ __device__ __forceinline__ u32x4 cursor_rsrc(const Cursor& c) {
   return r;
 }
 
-// Copy instruction j (of Geo::KINST) of this wave's share of the K tile at
-// the cursor; the lane's tile row is clamped to the run's last row.
+// Copy instruction j (of Geo::KINST) of this wave's share of the K or V tile
+// at the cursor; the lane's tile row is clamped to the run's last row.
 template <int D>
 __device__ __forceinline__ void copy_k(const Cursor& c, const LaneCopy& lc, int j, const char* kbuf,
                                        int wave) {
@@ -310,19 +296,47 @@ __device__ __forceinline__ void copy_k(const Cursor& c, const LaneCopy& lc, int 
   const int jx = (R == 4 ? j : (j & 1)) * 64;
   const int last = max(0, min(kBN, c.rows) - 1);
   const int row = min(blk * R + lc.kq, last);
-  copy16_to_lds(cursor_rsrc(c), 0u, (unsigned)(row * c.stride2 + (lc.kx16 ^ jx)),
+  copy16_to_lds(cursor_rsrc(c), 0u, __umul24((unsigned)row, (unsigned)c.stride2) + (unsigned)(lc.kx16 ^ jx),
                 (unsigned)(unsigned long long)(kbuf + blk * 1024));
 }
 
-// Copy instruction j (of Geo::VINST) of this wave's share of the V^T tile at
-// the cursor (8 channel rows of 64 keys per copy).
+// V tiles are only read by transposing reads, each of which takes 4 chunks
+// of 8 rows (4 r0 + a and 4 r0 + 8 + a, a < 4) with each half of the wave
+// on one group of 4 rows.  Their rows therefore take their own swizzle, one
+// that puts every half-wave's 16 slots on 16 distinct bank groups (no
+// conflict): 256-byte rows store chunk c of row r at slot c ^ g(r) with
+// g = ((r & 3) << 2) | ((r >> 2) & 3); 128-byte rows, two to a bank line,
+// at slot c ^ (4 ((r >> 1) & 1)).  Both depend on r % 16 only, as the K
+// swizzle does.  (The K swizzle would put 4 resp. 2 of a half-wave's slots
+// on one bank group.)
+template <int RB>
+__device__ __forceinline__ int swz_v(int r, int c) {
+  if constexpr (RB == 256) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  else return c ^ (((r >> 1) & 1) << 2);
+}
+
+// Copy instruction j (of Geo::KINST) of this wave's share of the V tile at
+// the cursor, rows swizzled by swz_v; the lane's tile row is clamped to the
+// run's last row.  A copy fills LDS block blk = wave * KINST + j, lane l
+// writing its 16 bytes at slot l % S of row l / S (S slots per row), so the
+// lane reads the source chunk that swz_v puts there.
 template <int D>
-__device__ __forceinline__ void copy_v(const Cursor& c, int qoff, const LaneCopy& lc, int j,
-                                       const char* vbuf, int wave) {
+__device__ __forceinline__ void copy_v(const Cursor& c, const LaneCopy& lc, int j, const char* vbuf, int wave) {
   using G = Geo<D>;
-  const int blk = wave * G::VINST + j;
-  copy16_to_lds(cursor_rsrc(c), (unsigned)(blk * 8 * c.stride2), (unsigned)(qoff + (lc.vx16 ^ ((j & 1) * 64))),
+  constexpr int R = 1024 / G::KRB;            // rows per copy
+  constexpr int S = G::KRB / 16;              // slots per row
+  const int blk = wave * G::KINST + j;
+  const int last = max(0, min(kBN, c.rows) - 1);
+  const int r = blk * R + lc.kq;              // tile row this lane fills
+  const int chunk = swz_v<G::KRB>(r, threadIdx.x & (S - 1));   // swz_v is its own inverse in c
+  copy16_to_lds(cursor_rsrc(c), 0u, __umul24((unsigned)min(r, last), (unsigned)c.stride2) + (unsigned)(chunk * 16),
                 (unsigned)(unsigned long long)(vbuf + blk * 1024));
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v(const Cursor& c, const LaneCopy& lc, char* vbuf, int wave) {
+#pragma unroll
+  for (int j = 0; j < Geo<D>::KINST; ++j) copy_v<D>(c, lc, j, vbuf, wave);
 }
 
 // The whole of this wave's share of one tile's copies at once (prologue).
@@ -331,12 +345,7 @@ __device__ __forceinline__ void issue_k(const Cursor& c, const LaneCopy& lc, cha
 #pragma unroll
   for (int j = 0; j < Geo<D>::KINST; ++j) copy_k<D>(c, lc, j, kbuf, wave);
 }
-template <int D>
-__device__ __forceinline__ void issue_v(const Cursor& c, const LaneCopy& lc, char* vbuf, int wave) {
-  const int qoff = lc.vq * c.stride2;
-#pragma unroll
-  for (int j = 0; j < Geo<D>::VINST; ++j) copy_v<D>(c, qoff, lc, j, vbuf, wave);
-}
+
 
 // Scores of one tile per (query block, 32-key half), and the bf16
 // probabilities of one tile per (query block, 16-key chunk).
@@ -527,14 +536,47 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   }
 }
 
+// One transposing LDS read (gfx950 ds_read_b64_tr_b16).  Each lane gives
+// the address of 8 bytes (four 16-bit elements); within each group of 16
+// lanes, lane i receives element i % 4 of the 8 bytes addressed by lane
+// 4k + i / 4 of its group as its element k (k = 0..3).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
+}
+
 // Output wave: constants of its 64 rows and its share of the tile copies.
 template <int D>
 struct OutCtx {
-  int voff[4];    // LDS byte offsets of this lane's V^T fragments
-  LaneCopy lc;    // per-lane parts of the tile copy addresses
-  int w;          // index among the output waves (its share of each copy)
+  int voff[2][D / 32];   // LDS byte offsets of this lane's two transposing reads per 32-channel block
+  LaneCopy lc;           // per-lane parts of the tile copy addresses
+  int w;                 // index among the output waves (its share of each copy)
   int lane;
 };
+
+// LDS byte offsets, for 16-key chunk 0 of a row-major V tile, of lane l's two
+// transposing reads of channel block db: together they give lane l the A
+// operand of O^T += V^T P^T, channel 32 db + l % 32 at keys 8 (l / 32) + 0..7.
+// Lane l = 16 G + i addresses row 8 (G / 2) + 4 t + i / 4 (read t = 0, 1),
+// channels 32 db + 16 (G % 2) + 4 (i % 4) .. + 3, so lane i of the group
+// receives channel 32 db + 16 (G % 2) + i at the four keys of read t.  Rows
+// are swizzled in 16-byte slots as the copies wrote them (swz_v); the
+// swizzle of row 16 c + r equals that of row r, so chunk c adds c * 16 rows.
+template <int D>
+__device__ __forceinline__ void v_read_offsets(int lane, int (&voff)[2][D / 32]) {
+  constexpr int KRB = 2 * D;
+  const int G = lane >> 4, i = lane & 15;
+  const int rbase = 8 * (G >> 1) + (i >> 2);
+  const int cbase = 16 * (G & 1) + 4 * (i & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int r = 4 * t + rbase;
+      const int col = 32 * db + cbase;
+      voff[t][db] = r * KRB + swz_v<KRB>(r, col >> 3) * 16 + (col & 7) * 2;
+    }
+}
 
 // One output-wave iteration: copies of V(i-1) (to vload; empty for i = 0)
 // and K(i+2) (to kload), then O = O * alpha(i-2) + V(i-2) P(i-2) from vread,
@@ -551,14 +593,21 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
   asm volatile("" : "+s"(i));
   wait_vm<G::KINST>();
   __syncthreads();
-  constexpr int NB = 4 * NDB;   // V^T fragments (kc, db)
+  constexpr int NB = 4 * NDB;   // V^T fragments (16-key chunk, 32-channel block)
   constexpr int RING = 4;
   if (i >= 2) {
     // The rescale flag, P(i-2) and the first V^T fragments are all in
     // flight before the flag is looked at.
     const int moved = *fread;
     auto vfrag = [&](int n) {
-      return *(const bf16x8*)(vread + cx.voff[n / NDB] + (n % NDB) * 32 * 128);
+      const char* base = vread + (n / NDB) * 16 * G::KRB;
+      union {
+        s16x4 h[2];
+        bf16x8 v;
+      } f;
+      f.h[0] = lds_read_tr16(base + cx.voff[0][n % NDB]);
+      f.h[1] = lds_read_tr16(base + cx.voff[1][n % NDB]);
+      return f.v;
     };
     bf16x8 pf[2][4];
 #pragma unroll
@@ -588,11 +637,10 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
       for (int qb = 0; qb < 2; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ch], o[qb][db], 0, 0, 0);
       // The tile copies go out one per MFMA pair: V(i-1), then K(i+2).
-      if (n >= 1 && n < 1 + G::VINST) copy_v<D>(vc, cx.lc.vq * vc.stride2, cx.lc, n - 1, vload, cx.w);
-      if (n == G::VINST) cursor_next<D, false>(vc, run);
-      if (n >= 1 + G::VINST && n < 1 + G::VINST + G::KINST)
-        copy_k<D>(kc, cx.lc, n - 1 - G::VINST, kload, cx.w);
-      if (n == G::VINST + G::KINST) cursor_next<D, true>(kc, run);
+      if (n >= 1 && n < 1 + G::KINST) copy_v<D>(vc, cx.lc, n - 1, vload, cx.w);
+      if (n == G::KINST) cursor_next<D, false>(vc, run);
+      if (n >= 1 + G::KINST && n < 1 + 2 * G::KINST) copy_k<D>(kc, cx.lc, n - 1 - G::KINST, kload, cx.w);
+      if (n == 2 * G::KINST) cursor_next<D, true>(kc, run);
     }
   } else {
     // Nothing to add yet; V(-1) is empty.
@@ -632,12 +680,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NC = G::NC;
   constexpr int NDB = G::NDB;
   constexpr int KRB = G::KRB;
-  __shared__ __attribute__((aligned(1024))) char sK[kKSlots * G::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV[kVSlots * G::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sP[2 * kPairs * kPBytes];
-  __shared__ float sAlpha[2 * kPairs * 64];
-  __shared__ int sFlag[2 * kPairs];
-  __shared__ float sL[kPairs * 64];
+  // One LDS block laid out by hand with the V ring at address 0: a V read is
+  // then its lane's offset plus an immediate (slot, 16-key chunk), which the
+  // 16-bit offset field of an LDS read holds, so the output wave spends no
+  // vector instruction on V addresses.
+  constexpr int kOffK = kVSlots * G::KBYTES;
+  constexpr int kOffP = kOffK + kKSlots * G::KBYTES;
+  constexpr int kOffA = kOffP + 2 * kPairs * kPBytes;
+  constexpr int kOffF = kOffA + 2 * kPairs * 64 * (int)sizeof(float);
+  constexpr int kOffL = kOffF + 2 * kPairs * (int)sizeof(int);
+  constexpr int kLdsBytes = kOffL + kPairs * 64 * (int)sizeof(float);
+  static_assert(kVSlots * G::KBYTES <= 65536, "V reads take their slot and chunk as an immediate");
+  static_assert(kOffP % 1024 == 0 && kOffK % 1024 == 0, "tiles stay 1 KB aligned");
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char* const sV = smem;
+  char* const sK = smem + kOffK;
+  char* const sP = smem + kOffP;
+  float* const sAlpha = (float*)(smem + kOffA);
+  int* const sFlag = (int*)(smem + kOffF);
+  float* const sL = (float*)(smem + kOffL);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -793,8 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     cx.lane = lane;
     cx.w = wave - kPairs;
     cx.lc = lane_copy<D>(lane);
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) cx.voff[kc] = col * 128 + swz<128>(col, 2 * kc + hi) * 16;
+    v_read_offsets<D>(lane, cx.voff);
     f32x16 o[2][NDB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -816,7 +876,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     // slot (i+2) % 3; reads V(i-2) from slot i % 2 and P(i-2) from buffer i % 2.
     int k3 = 2;   // (i + 2) % 3
     char* const v0 = sV;
-    char* const v1 = sV + G::VBYTES;
+    char* const v1 = sV + G::KBYTES;
     const char* const p0 = sP + pair * kPBytes;
     const char* const p1 = sP + (kPairs + pair) * kPBytes;
     const float* const a0 = sAlpha + pair * 64;

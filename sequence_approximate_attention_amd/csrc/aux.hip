@@ -1,4 +1,4 @@
-// Data-movement kernels: passing-block gather, key-contiguous V copy, LSE merge.
+// Data-movement kernels: passing-block gather and LSE merge.
 #include "spava_common.h"
 
 namespace spava {
@@ -35,80 +35,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
   const uint8_t* src = (which ? v : k) + tok * kv_st_bytes + g * kv_sh_bytes + c * 16;
   uint8_t* dst = (which ? vp : kp) + ri * row_bytes + c * 16;
   *(uint4*)dst = *(const uint4*)src;
-}
-
-// ---------------------------------------------------------------------------
-// Key-contiguous copy of V for the bf16 attention kernel (V^T per KV head).
-// Tile = 64 key positions x D channels, transposed through LDS.  Padding key
-// positions are written as zeros (their probabilities are masked to 0, and
-// 0 * 0 keeps the PV product finite).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void vtranspose_kernel(AttnArgs a, uint16_t* __restrict__ vt,
-                                                         uint16_t* __restrict__ vpt, int tile0) {
-  constexpr int TS = kKeyTile + 2;  // LDS row stride (elements) of the [D][keys] tile
-  __shared__ uint16_t sT[D * TS];
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int main_tiles = a.vl.main_len / kKeyTile;
-  const int tt = tile0 + blockIdx.x;
-  const bool pass = tt >= main_tiles;
-  const int p0 = (pass ? tt - main_tiles : tt) * kKeyTile;
-
-  // Which source rows feed this tile.
-  long src_row0 = 0;   // element offset of key 0 of the run in v / vp
-  long src_stride = 0; // elements between keys
-  int n_valid = 0;     // keys of the tile that exist
-  const uint16_t* src = nullptr;
-  if (pass) {
-    src = (const uint16_t*)a.vp;
-    const int total = a.V * a.lp;
-    n_valid = max(0, min(kKeyTile, total - p0));
-    src_row0 = ((long)g * total + p0) * D;
-    src_stride = D;
-  } else {
-    src = (const uint16_t*)a.v;
-    int tok0, len, off;
-    if (p0 < a.vl.off_block0) {
-      tok0 = 0; len = a.la; off = p0;
-    } else if (p0 < a.vl.off_query) {
-      const int h = (p0 - a.vl.off_block0) / a.vl.pad_block;
-      off = (p0 - a.vl.off_block0) % a.vl.pad_block;
-      tok0 = a.la + h * a.L; len = a.L;
-    } else {
-      off = p0 - a.vl.off_query;
-      tok0 = a.la + a.V * a.L; len = a.nq;
-    }
-    n_valid = max(0, min(kKeyTile, len - off));
-    src_stride = a.kv_st;
-    src_row0 = (long)(tok0 + off) * src_stride + (long)g * a.kv_sh;
-  }
-
-  constexpr int CPR = D / 8;
-  for (int ch = tid; ch < kKeyTile * CPR; ch += 256) {
-    const int key = ch / CPR;
-    const int c = ch % CPR;
-    union { uint4 u; uint16_t h[8]; } x;
-    if (key < n_valid) {
-      x.u = *(const uint4*)(src + src_row0 + (long)key * src_stride + c * 8);
-    } else {
-      x.u = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sT[(c * 8 + e) * TS + key] = x.h[e];
-  }
-  __syncthreads();
-  const int rowlen = pass ? a.vl.pass_len : a.vl.main_len;
-  uint16_t* dst = (pass ? vpt : vt) + (long)g * D * rowlen + p0;
-  for (int ch = tid; ch < D * (kKeyTile / 8); ch += 256) {
-    const int d = ch / (kKeyTile / 8);
-    const int kc = ch % (kKeyTile / 8);
-    union { uint4 u; uint32_t w[4]; } y;
-    const uint16_t* s = sT + d * TS + kc * 8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y.w[e] = (uint32_t)s[2 * e] | ((uint32_t)s[2 * e + 1] << 16);
-    *(uint4*)(dst + (long)d * rowlen + kc * 8) = y.u;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -213,20 +139,6 @@ hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void*
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint8_t*)k,
                      (const uint8_t*)v, idx, (uint8_t*)kp, (uint8_t*)vp, la, V, L, Hkv, lp,
                      row_bytes, kv_st_bytes, kv_sh_bytes, total);
-  return hipGetLastError();
-}
-
-hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, int phase, hipStream_t s) {
-  const int main_tiles = a.vl.main_len / kKeyTile;
-  const int pass_tiles = a.vl.pass_len / kKeyTile;
-  const int tile0 = phase == kPhasePassing ? main_tiles : 0;
-  const int tiles = (phase == kPhaseLocal ? 0 : pass_tiles) + (phase == kPhasePassing ? 0 : main_tiles);
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles, a.Hkv);
-  if (a.D == 128)
-    hipLaunchKernelGGL((vtranspose_kernel<128>), grid, dim3(256), 0, s, a, vt, vpt, tile0);
-  else
-    hipLaunchKernelGGL((vtranspose_kernel<64>), grid, dim3(256), 0, s, a, vt, vpt, tile0);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKeyTile = 64;      // keys per attention tile; V^T segments pad to it
+constexpr int kKeyTile = 64;      // keys per attention tile
 constexpr int kRowsPerWave = 32;  // query rows per wave (MFMA 32x32 column block)
 
 enum UnitKind : int {
@@ -32,38 +32,13 @@ enum UnitKind : int {
 inline __host__ __device__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline __host__ __device__ int round_up(int a, int b) { return ceil_div(a, b) * b; }
 
-// Offsets of the padded, key-contiguous V copy ("V^T") kept in the attention
-// workspace: per KV head g and channel c, one row of keys laid out as
-//   [anchor | block 0 | ... | block V-1 | query], each padded to kKeyTile
-// with zeros, then the passing values [h=0..V-1][t] padded to kKeyTile.
-struct VtLayout {
-  int pad_anchor, pad_block, pad_query;  // padded segment lengths
-  int off_block0, off_query;             // offsets inside a main row
-  int main_len;                          // padded keys per main row
-  int pass_len;                          // padded passing keys per row
-  __host__ __device__ static VtLayout make(int la, int V, int L, int nq, int lp) {
-    VtLayout t;
-    t.pad_anchor = round_up(la, kKeyTile);
-    t.pad_block = round_up(L, kKeyTile);
-    t.pad_query = round_up(nq, kKeyTile);
-    t.off_block0 = t.pad_anchor;
-    t.off_query = t.pad_anchor + V * t.pad_block;
-    t.main_len = t.off_query + t.pad_query;
-    t.pass_len = round_up(V * lp, kKeyTile);
-    if (t.pass_len == 0) t.pass_len = kKeyTile;
-    return t;
-  }
-};
-
 // Everything an attention launch needs (passed by value as the kernel argument).
 struct AttnArgs {
   const void* q;
   const void* k;
-  const void* v;       // row-major V (float32 path)
+  const void* v;
   const void* kp;
-  const void* vp;      // row-major passing V (float32 path)
-  const uint16_t* vt;  // key-contiguous V (bf16 path)
-  const uint16_t* vpt; // key-contiguous passing V (bf16 path)
+  const void* vp;
   void* o;
   float* lse;
   float* o_part;
@@ -74,7 +49,6 @@ struct AttnArgs {
   long kv_st, kv_sh;   // the same for k and v
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
-  VtLayout vl;
   // Unit ranges, in launch order (see unit_decode):
   int n_ctx_units_per_host;  // ceil(L/BM) * Hq
   int n_q_units;             // ceil(nq*G/BM) * Hkv, per query partial
@@ -191,9 +165,7 @@ struct Seg {
   int kind;        // 0: rows of k (token-major, stride Hkv*D); 1: rows of kp
   long k_off;      // element offset of key 0 of the segment in k or kp
   long k_stride;   // elements between consecutive keys
-  long vt_off;     // element offset of key 0 in the V^T row of channel 0 (bf16 path)
-  int vt_pass;     // 1: segment lives in the passing V^T rows
-  long v_off;      // element offset of key 0 in v or vp (float32 path)
+  long v_off;      // element offset of key 0 in v or vp
   long v_stride;
   int len;         // number of keys
   int causal;      // 1: key token (tok0 + j) must be <= query token
@@ -204,13 +176,11 @@ struct Seg {
 __device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
   const int g = u.group;
   int n = 0;
-  auto main_seg = [&](int tok0, int len, int vt_key_off, int causal) {
+  auto main_seg = [&](int tok0, int len, int causal) {
     Seg x;
     x.kind = 0;
     x.k_off = (long)tok0 * a.kv_st + (long)g * a.kv_sh;
     x.k_stride = a.kv_st;
-    x.vt_off = (long)g * a.D * a.vl.main_len + vt_key_off;
-    x.vt_pass = 0;
     x.v_off = x.k_off;
     x.v_stride = a.kv_st;
     x.len = len;
@@ -220,17 +190,15 @@ __device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
   };
   switch (u.kind) {
     case kAnchor:
-      main_seg(0, a.la, 0, 1);
+      main_seg(0, a.la, 1);
       break;
     case kContext: {
-      if (a.la > 0) main_seg(0, a.la, 0, 0);
+      if (a.la > 0) main_seg(0, a.la, 0);
       if (u.host > 0 && a.lp > 0) {
         Seg x;
         x.kind = 1;
         x.k_off = (long)g * a.V * a.lp * a.D;
         x.k_stride = a.D;
-        x.vt_off = (long)g * a.D * a.vl.pass_len;
-        x.vt_pass = 1;
         x.v_off = x.k_off;
         x.v_stride = a.D;
         x.len = u.host * a.lp;
@@ -239,16 +207,16 @@ __device__ inline int unit_segments(const AttnArgs& a, const Unit& u, Seg* s) {
         s[n++] = x;
       }
       const int b0 = a.la + u.host * a.L;
-      main_seg(b0, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 1);
+      main_seg(b0, a.L, 1);
       break;
     }
     case kQueryHead: {
-      if (a.la > 0) main_seg(0, a.la, 0, 0);
-      main_seg(a.la + a.V * a.L, a.nq, a.vl.off_query, 1);
+      if (a.la > 0) main_seg(0, a.la, 0);
+      main_seg(a.la + a.V * a.L, a.nq, 1);
       break;
     }
     case kQueryBlock:
-      main_seg(a.la + u.host * a.L, a.L, a.vl.off_block0 + u.host * a.vl.pad_block, 0);
+      main_seg(a.la + u.host * a.L, a.L, 0);
       break;
   }
   return n;
@@ -301,9 +269,6 @@ int attn_bf16_rows_per_unit();   // query rows per workgroup of the bf16 kernel
 hipError_t launch_score_bf16(const AttnArgs& a, void* ws, float* scores, hipStream_t s);
 size_t score_bf16_ws_bytes(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
-// V^T copy of the main rows (phase all / local) and of the passing values
-// (phase all / passing).
-hipError_t launch_vtranspose(const AttnArgs& a, uint16_t* vt, uint16_t* vpt, int phase, hipStream_t s);
 hipError_t launch_rowstat_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_colsum_f32(const AttnArgs& a, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, int32_t* idx, int n_lists, int L, int lp, hipStream_t s);

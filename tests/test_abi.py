@@ -34,7 +34,7 @@ def test_plan_struct_matches_the_header():
 
 
 def test_version_and_empty_error():
-    assert S.lib().spava_version() == 100
+    assert S.lib().spava_version() == 200
     assert isinstance(S.lib().spava_last_error(), bytes)
 
 
@@ -68,6 +68,18 @@ def plan(**kw):
     (dict(q_stride_head=1 << 26), S.SPAVA_OK),
     (dict(q_stride_head=1 << 31), S.SPAVA_EINVAL),
     (dict(kv_stride_tok=1 << 22), S.SPAVA_EINVAL),
+    # a token stride shorter than a row would overlap the next token's row
+    (dict(kv_stride_tok=32, kv_stride_head=64), S.SPAVA_EINVAL),
+    (dict(q_stride_tok=48), S.SPAVA_EINVAL),
+    (dict(kv_stride_tok=64, kv_stride_head=2 * 64), S.SPAVA_OK),
+    # token strides stay below 2^24 bytes (tiny plans, so that no extent
+    # check is what rejects them)
+    (dict(n_anchor=0, n_hosts=1, host_len=2, n_query=1, lp=0, dtype=S.SPAVA_BF16,
+          kv_stride_tok=(1 << 23) - 8), S.SPAVA_OK),
+    (dict(n_anchor=0, n_hosts=1, host_len=2, n_query=1, lp=0, dtype=S.SPAVA_BF16,
+          kv_stride_tok=1 << 23), S.SPAVA_EINVAL),
+    (dict(n_anchor=0, n_hosts=1, host_len=2, n_query=1, lp=0, dtype=S.SPAVA_F32,
+          q_stride_tok=1 << 22), S.SPAVA_EINVAL),
 ])
 def test_plan_check(kw, code):
     assert S.spava_plan_check(plan(**kw)) == code
@@ -98,11 +110,6 @@ def test_workspace_sizes():
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4 + sc(128)
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4 + sc(128)
     assert S.spava_score_topk_context_ws_bytes(plan(lp=999)) == 0
-    # key-contiguous V: Hkv * d * (pad(la) + V*pad(L) + pad(n_q)) + passing, bf16
-    main = 1 * 128 * (64 + 4 * 128 + 64) * 2
-    pas = 1 * 128 * 64 * 2
-    assert S.spava_attn_fwd_ws_bytes(p) == main + pas
-    assert S.spava_attn_fwd_ws_bytes(plan(lp=999)) == 0
 
 
 def test_null_and_misaligned_pointers_rejected_on_host():
@@ -125,11 +132,11 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     assert lib.spava_score_topk(ctypes.byref(p), fake, fake, None, fake, fake, need - 1, None) == S.SPAVA_EWORKSPACE
     assert lib.spava_gather_passing(ctypes.byref(p), fake, None, fake, fake, fake, None) == S.SPAVA_EINVAL
     assert lib.spava_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
-                              fake, 1 << 20, None) == S.SPAVA_EINVAL
+                              None) == S.SPAVA_EINVAL
     pb = plan(dtype=S.SPAVA_BF16).c()
-    assert lib.spava_attn_fwd(ctypes.byref(pb), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                              fake, 16, None) == S.SPAVA_EWORKSPACE
-    assert b"workspace" in lib.spava_last_error()
+    assert lib.spava_attn_fwd(ctypes.byref(pb), fake, odd, fake, fake, fake, fake, fake, fake, fake,
+                              None) == S.SPAVA_EINVAL
+    assert b"aligned" in lib.spava_last_error()
     assert lib.spava_lse_merge(0, 4, 2, 64, fake, fake, fake, 128, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
     assert lib.spava_lse_merge(2, 4, 2, 62, fake, fake, fake, 128, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
     assert lib.spava_lse_merge(2, 4, 2, 64, fake, fake, fake, 64, fake, 4, S.SPAVA_F32, None) == S.SPAVA_EINVAL
@@ -157,14 +164,12 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     # Attention in phases: unknown phase; the LOCAL phase needs no passing
     # blocks but its partials, the PASSING phase the reverse.
     assert lib.spava_attn_fwd_phase(ctypes.byref(p), 7, fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                                    fake, 1 << 20, None) == S.SPAVA_EINVAL
+                                    None) == S.SPAVA_EINVAL
     assert b"phase" in lib.spava_last_error()
     assert lib.spava_attn_fwd_phase(ctypes.byref(p), S.SPAVA_PHASE_LOCAL, fake, fake, fake, None, None, fake, fake,
-                                    None, fake, fake, 1 << 20, None) == S.SPAVA_EINVAL
+                                    None, fake, None) == S.SPAVA_EINVAL
     assert lib.spava_attn_fwd_phase(ctypes.byref(p), S.SPAVA_PHASE_PASSING, fake, fake, fake, None, fake, fake,
-                                    fake, None, None, fake, 1 << 20, None) == S.SPAVA_EINVAL
-    assert lib.spava_attn_fwd_phase(ctypes.byref(pb), S.SPAVA_PHASE_PASSING, fake, fake, fake, fake, fake, fake,
-                                    fake, None, None, fake, 16, None) == S.SPAVA_EWORKSPACE
+                                    fake, None, None, None) == S.SPAVA_EINVAL
     # Scores from the query partials: lse_part is required when n_query > 0.
     assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, fake, None, fake, fake, None) == S.SPAVA_EINVAL
     assert lib.spava_score_topk_from_partials(ctypes.byref(p), fake, odd, fake, fake, fake, None) == S.SPAVA_EINVAL

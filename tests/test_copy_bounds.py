@@ -23,14 +23,6 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def vt_layout(la, V, L, nq, lp):
-    pad = lambda n: cdiv(n, KT) * KT
-    off_block0 = pad(la)
-    off_query = pad(la) + V * pad(L)
-    return dict(pad_block=pad(L), off_block0=off_block0, off_query=off_query,
-                main_len=off_query + pad(nq), pass_len=pad(V * lp) or KT)
-
-
 class Extent:
     def __init__(self, name, nbytes):
         self.name, self.nbytes = name, nbytes
@@ -56,17 +48,17 @@ def layout(w, D, strides):
 
 
 def attention_copies(w, D, past_walk="stay", strides=None):
-    """Walk the attention kernel's K and V^T cursors of every unit.  With
+    """Walk the attention kernel's K and V cursors of every unit (V tiles are
+    copied row-major from v and vp exactly as K tiles from k and kp).  With
     past_walk="advance" a cursor keeps stepping over whole tiles after the
     walk (what a cursor whose remaining byte count had gone negative, read as
     an unsigned range, would do); the kernels keep it on its last tile."""
     la, V, L, nq, lp, Hq, Hkv = w.n_anchor, w.n_hosts, w.host_len, w.n_query, w.lp, w.n_q_heads, w.n_kv_heads
     G = Hq // Hkv
     N = la + V * L + nq
-    vl = vt_layout(la, V, L, nq, lp)
     (_, _, kv_st, kv_sh), _, k_ext = layout(w, D, strides)
     ext = {"k": Extent("k", k_ext * 2), "kp": Extent("kp", Hkv * V * lp * D * 2),
-           "vt": Extent("vt", Hkv * D * vl["main_len"] * 2), "vpt": Extent("vpt", Hkv * D * vl["pass_len"] * 2)}
+           "v": Extent("v", k_ext * 2), "vp": Extent("vp", Hkv * V * lp * D * 2)}
     n_ctx_h = cdiv(L, BM) * Hq
     n_q = cdiv(nq * G, BM) * Hkv
     qt = n_q // Hkv
@@ -99,22 +91,20 @@ def attention_copies(w, D, past_walk="stay", strides=None):
             continue
         gmax = max(toks)
 
-        def main(tok0, n, vkey, causal):
-            return dict(kbuf="k", k=(tok0 * kv_st + g * kv_sh) * 2, vbuf="vt", vt=(g * D * vl["main_len"] + vkey) * 2,
-                        kstr=kv_st * 2, vstr=vl["main_len"] * 2, len=n, causal=causal, tok0=tok0)
-        runs = [main(0, 0, 0, 0)] * 3
+        def main(tok0, n, causal):
+            return dict(kbuf="k", k=(tok0 * kv_st + g * kv_sh) * 2, vbuf="v", v=(tok0 * kv_st + g * kv_sh) * 2,
+                        kstr=kv_st * 2, len=n, causal=causal, tok0=tok0)
+        runs = [main(0, 0, 0)] * 3
         if kind == "anchor":
-            runs = [main(0, la, 0, 1), dict(runs[1], len=0), dict(runs[2], len=0)]
+            runs = [main(0, la, 1), dict(runs[1], len=0), dict(runs[2], len=0)]
         elif kind == "ctx":
-            pas = dict(kbuf="kp", k=g * V * lp * D * 2, vbuf="vpt", vt=g * D * vl["pass_len"] * 2,
-                       kstr=D * 2, vstr=vl["pass_len"] * 2, len=host * lp if lp else 0, causal=0, tok0=0)
-            runs = [main(0, la, 0, 0), pas if host > 0 else dict(pas, len=0),
-                    main(la + host * L, L, vl["off_block0"] + host * vl["pad_block"], 1)]
+            pas = dict(kbuf="kp", k=g * V * lp * D * 2, vbuf="vp", v=g * V * lp * D * 2,
+                       kstr=D * 2, len=host * lp if lp else 0, causal=0, tok0=0)
+            runs = [main(0, la, 0), pas if host > 0 else dict(pas, len=0), main(la + host * L, L, 1)]
         elif kind == "qhead":
-            runs = [main(0, la, 0, 0), main(la + V * L, nq, vl["off_query"], 1), dict(runs[2], len=0)]
+            runs = [main(0, la, 0), main(la + V * L, nq, 1), dict(runs[2], len=0)]
         else:
-            runs = [main(la + host * L, L, vl["off_block0"] + host * vl["pad_block"], 0),
-                    dict(runs[1], len=0), dict(runs[2], len=0)]
+            runs = [main(la + host * L, L, 0), dict(runs[1], len=0), dict(runs[2], len=0)]
         nts = []
         for x in runs:
             n = min(x["len"], gmax - x["tok0"] + 1) if x["causal"] else x["len"]
@@ -122,10 +112,11 @@ def attention_copies(w, D, past_walk="stay", strides=None):
         T = sum(nts)
 
         def walk(is_k):
-            """Byte ranges [lo, hi) and buffer of the copies issued for tiles 0 .. T+3."""
+            """Byte ranges [lo, hi) and buffer of the copies issued for tiles
+            0 .. T+3 of the K (is_k) or V cursor: both walk the same rows, K
+            from k / kp and V from v / vp."""
             out = []
-            addr, stride, buf = ((runs[0]["k"], runs[0]["kstr"], "k") if is_k
-                                 else (runs[0]["vt"], runs[0]["vstr"], "vt"))
+            addr, stride, buf = runs[0]["k" if is_k else "v"], runs[0]["kstr"], "k" if is_k else "v"
             s, left, rows = 0, 0, 0
 
             def enter(s0):
@@ -141,24 +132,16 @@ def attention_copies(w, D, past_walk="stay", strides=None):
                     return
                 x = runs[s]
                 left = nts[s]
-                if is_k:
-                    addr, stride, buf, rows = x["k"], x["kstr"], x["kbuf"], x["len"]
-                else:
-                    addr, stride, buf = x["vt"], x["vstr"], x["vbuf"]
+                addr, stride, rows = (x["k"] if is_k else x["v"]), x["kstr"], x["len"]
+                buf = x["kbuf"] if is_k else x["vbuf"]
             enter(0)
             for _ in range(T + 4):
-                if is_k:
-                    last = max(0, min(KT, rows) - 1)
-                    out.append((buf, addr, addr + last * stride + D * 2))
-                else:
-                    out.append((buf, addr, addr + (D - 1) * stride + KT * 2))
+                last = max(0, min(KT, rows) - 1)
+                out.append((buf, addr, addr + last * stride + D * 2))
                 if left > 1:
                     left -= 1
-                    if is_k:
-                        addr += KT * stride
-                        rows -= KT
-                    else:
-                        addr += KT * 2
+                    addr += KT * stride
+                    rows -= KT
                 else:
                     enter(s + 1)
             return out

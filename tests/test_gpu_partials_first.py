@@ -74,15 +74,14 @@ def test_phases_write_disjoint_rows():
     S.spava_gather_passing(plan, k, v, b.idx, b.kp, b.vp)
     for t in (b.o, b.lse, b.o_part, b.lse_part):
         t.fill_(float("nan"))
-    S.spava_attn_fwd_phase(plan, S.SPAVA_PHASE_LOCAL, q, k, v, b.kp, b.vp, b.o, b.lse, b.o_part, b.lse_part,
-                           b.ws_attn)
+    S.spava_attn_fwd_phase(plan, S.SPAVA_PHASE_LOCAL, q, k, v, b.kp, b.vp, b.o, b.lse, b.o_part, b.lse_part)
     torch.cuda.synchronize()
     h1 = w.n_anchor + w.host_len            # first row of host 1
     q0 = w.n_anchor + w.n_hosts * w.host_len
     assert not torch.isnan(b.o[:h1].float()).any() and not torch.isnan(b.lse[:, :h1]).any()
     assert torch.isnan(b.o[h1:q0].float()).all() and torch.isnan(b.lse[:, h1:q0]).all()
     assert not torch.isnan(b.o_part).any() and not torch.isnan(b.lse_part).any()
-    S.spava_attn_fwd_phase(plan, S.SPAVA_PHASE_PASSING, q, k, v, b.kp, b.vp, b.o, b.lse, None, None, b.ws_attn)
+    S.spava_attn_fwd_phase(plan, S.SPAVA_PHASE_PASSING, q, k, v, b.kp, b.vp, b.o, b.lse, None, None)
     torch.cuda.synchronize()
     assert not torch.isnan(b.o[:q0].float()).any() and not torch.isnan(b.lse[:, :q0]).any()
 
