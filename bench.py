@@ -293,27 +293,45 @@ def main():
                                                 bufs.o_part, bufs.lse_part, stream)
     rec = lambda ev, i: ev[i].record(stream) if ev is not None else None
 
+    merge = lambda: S.spava_lse_merge(bufs.o_part, bufs.lse_part, bufs.o[q0:], plan.n_q_heads * plan.head_dim,
+                                      bufs.lse[:, q0:], plan.n_tokens, stream)
+    # Events around the calls of a step and the spans (pairs of events) that
+    # make up each stage.  One pass: score | gather | attention | merge.
+    # Figure 5 order: LOCAL phase | scores from the query partials | gather |
+    # PASSING phase | merge.  (Merging right after the LOCAL phase, while its
+    # partials are freshly written, measured slower: 59.7 against 56.1 us.)
+    SPANS = {
+        "one-pass": {"score_topk": [(0, 1)], "gather": [(1, 2)], "attn_fwd": [(2, 3)], "lse_merge": [(3, 4)],
+                     "step": [(0, 4)]},
+        "partials-first": {"attn_fwd": [(0, 1), (3, 4)], "score_topk": [(1, 2)], "gather": [(2, 3)],
+                           "lse_merge": [(4, 5)], "step": [(0, 5)]},
+    }[args.order]
+    N_EV = 6
+    span_ms = lambda ev, name: sum(ev[a].elapsed_time(ev[b]) for a, b in SPANS[name])
+
     def step(ev=None):
-        # events: 0 | score | 1 | gather | 2 | attention | 3 | merge | 4; in the
-        # partials-first order the attention is split around score + gather
-        # (local phase between 5 and 0, passing phase between 2 and 3).
         if args.order == "partials-first":
-            rec(ev, 5)
-            attn(S.SPAVA_PHASE_LOCAL)
             rec(ev, 0)
+            attn(S.SPAVA_PHASE_LOCAL)
+            rec(ev, 1)
             S.spava_score_topk_from_partials(plan, q, k, bufs.lse_part, bufs.scores, bufs.idx, stream)
+            rec(ev, 2)
+            S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
+            rec(ev, 3)
+            attn(S.SPAVA_PHASE_PASSING)
+            rec(ev, 4)
+            merge()
+            rec(ev, 5)
         else:
             rec(ev, 0)
             score_topk(plan, q, k, bufs.scores, bufs.idx, ws_score, stream)
-        rec(ev, 1)
-        S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
-        rec(ev, 2)
-        attn(S.SPAVA_PHASE_PASSING if args.order == "partials-first" else S.SPAVA_PHASE_ALL)
-        rec(ev, 3)
-        S.spava_lse_merge(bufs.o_part, bufs.lse_part, bufs.o[q0:], plan.n_q_heads * plan.head_dim,
-                          bufs.lse[:, q0:], plan.n_tokens, stream)
-        if ev is not None:
-            ev[4].record(stream)
+            rec(ev, 1)
+            S.spava_gather_passing(plan, k, v, bufs.idx, bufs.kp, bufs.vp, stream)
+            rec(ev, 2)
+            attn(S.SPAVA_PHASE_ALL)
+            rec(ev, 3)
+            merge()
+            rec(ev, 4)
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
@@ -325,7 +343,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(N_EV)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -340,15 +358,13 @@ def main():
     cold = None
     if args.cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.cold_steps)]
+        cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(N_EV)] for _ in range(args.cold_steps)]
         for i in range(args.cold_steps):
             flush.fill_(i & 255)
             step(cold_ev[i])
         torch.cuda.synchronize()
-        step_ms = [ev[0].elapsed_time(ev[4]) + (ev[5].elapsed_time(ev[0]) if args.order == "partials-first" else 0.0)
-                   for ev in cold_ev]
-        attn_cold = [ev[2].elapsed_time(ev[3]) + (ev[5].elapsed_time(ev[0]) if args.order == "partials-first" else 0.0)
-                     for ev in cold_ev]
+        step_ms = [span_ms(ev, "step") for ev in cold_ev]
+        attn_cold = [span_ms(ev, "attn_fwd") for ev in cold_ev]
         cold = {"steps": args.cold_steps, "flush_mb": 512, "ms_per_step_median": float(np.median(step_ms)),
                 "attn_ms_median": float(np.median(attn_cold))}
         del flush
@@ -372,15 +388,7 @@ def main():
         dense_ms = float(np.median(dts))
         del db
 
-    stage = {"score_topk": [], "gather": [], "attn_fwd": [], "lse_merge": []}
-    for ev in events:
-        stage["score_topk"].append(ev[0].elapsed_time(ev[1]))
-        stage["gather"].append(ev[1].elapsed_time(ev[2]))
-        attn_ms_i = ev[2].elapsed_time(ev[3])
-        if args.order == "partials-first":
-            attn_ms_i += ev[5].elapsed_time(ev[0])
-        stage["attn_fwd"].append(attn_ms_i)
-        stage["lse_merge"].append(ev[3].elapsed_time(ev[4]))
+    stage = {kk: [span_ms(ev, kk) for ev in events] for kk in ("score_topk", "gather", "attn_fwd", "lse_merge")}
     stage_ms = {kk: float(np.mean(vv)) for kk, vv in stage.items()}
     # Per-step GPU time from the events (the four calls back to back).
     step_ev = [sum(stage[kk][i] for kk in stage) for i in range(args.steps)]
