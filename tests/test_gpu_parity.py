@@ -60,6 +60,9 @@ SMALL = [
     W.small_workload("bf16", Hq=4, Hkv=4, d=128, la=5, V=5, L=64, n_q=1, lp=1, seed=10),
     W.small_workload("bf16", Hq=2, Hkv=1, d=128, la=64, V=1, L=300, n_q=0, lp=17, seed=11),
     W.small_workload("f32", Hq=4, Hkv=2, d=128, la=40, V=3, L=90, n_q=12, lp=30, seed=12),
+    # d = 64 with walks of up to 27 key tiles (both V ring slots reused many
+    # times, ragged run ends inside tiles)
+    W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=300, V=3, L=1000, n_q=40, lp=200, seed=13),
 ]
 
 
