@@ -93,3 +93,10 @@ def test_qwen3b_32k_partials_first():
 def test_llama8b_128k_text_partials_first():
     w = W.LLAMA8B_128K_TEXT
     run_case(w, query_stride=11, stride=251, heads=[0, w.n_q_heads - 1], partials_first=True)
+
+
+def test_qwen7b_256k_frames_partials_first():
+    # The benchmark's default configuration (the 256K frame shape in this
+    # order): every score and index; attention on one query head of every
+    # KV group and the last head, every 251st token.
+    run_case(W.QWEN7B_256K, query_stride=17, stride=251, partials_first=True)
