@@ -22,11 +22,13 @@
 // are skipped.
 //
 //   colsum_kernel: combines each row's chunk partials into its log2-domain
-//     log-sum-exp, then for 256 keys per workgroup sums exp2(s - lse) over the
-//     rows of its row split.  Each wave keeps 64 keys' fragments in registers;
-//     the two halves of the workgroup (4 waves each) take alternate 32-row
-//     chunks, whose Q tiles are copied into a 3-slot LDS ring per half, two
-//     chunks ahead.  Column sums accumulate per chunk in float32, across
+//     log-sum-exp, then for 256 (query rows) or 384 (context selector) keys
+//     sums exp2(s - lse) over the rows of its row split.  Each of 4 waves
+//     keeps its 64 or 96 keys' fragments in registers; they walk the split's 32-row
+//     chunks, whose Q tiles are copied into a 3-slot LDS ring, two chunks
+//     ahead.  Large grids run such 4-wave workgroups two or three to a CU;
+//     small ones pair two of them in one workgroup on alternate chunks, their
+//     totals added at the end.  Column sums accumulate per chunk in float32, across
 //     chunks in float64, in a fixed order (deterministic).  The query rows
 //     form one split (the sums go straight to the scores); the context
 //     selector splits each head's tokens into ranges of at least 1024, each
@@ -258,13 +260,15 @@ __global__ __launch_bounds__(kRsThreads, 2) void rowstat_chunk_kernel(AttnArgs a
 // ---------------------------------------------------------------------------
 // Column sums.
 
-constexpr int kCsHalves = 2;
+// A workgroup is one or two halves of 4 waves over the same keys; the halves
+// take alternate 32-row chunks and add their totals at the end.  One half per
+// workgroup lets three workgroups (query rows, 155 VGPRs) or two (context
+// selector) share a CU independently, so one's exponentials overlap another's
+// MFMAs; two halves keep 8 waves per CU when the grid is too small for that.
 constexpr int kCsWavesPerHalf = 4;
-constexpr int kCsThreads = kCsHalves * kCsWavesPerHalf * 64;
 constexpr int kCsKbQuery = 2;                    // 32-key blocks per wave: query rows
-constexpr int kCsKbQueryWide = 3;                // ... query rows, grids of >= kCsWideGrid workgroups
-constexpr int kCsWideGrid = 1024;
 constexpr int kCsKbCtx = 3;                      // ... context selector
+constexpr int kCsSingleGrid = 1024;              // query rows: one half per workgroup from this grid size on
 constexpr int kCsRows = 32;                      // rows per chunk
 constexpr int kCsSlots = 3;                      // Q tile ring per half
 constexpr int kCsLseRows = 4096;                 // rows of the LSE table per pass
@@ -317,8 +321,8 @@ __device__ __forceinline__ void cs_issue(const AttnArgs& a, const u32x4& rs_q, i
   }
 }
 
-template <int D, bool CTX, int KB>
-__global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int KC,
+template <int D, bool CTX, int KB, int HALVES>
+__global__ __launch_bounds__(HALVES * kCsWavesPerHalf * 64, HALVES == 2 ? 1 : (CTX ? 2 : 3)) void colsum_kernel(AttnArgs a, int KC,
                                                                const float2* __restrict__ part,
                                                                float* __restrict__ scores,
                                                                float* __restrict__ cpart, int splits_per_head,
@@ -326,9 +330,10 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   using G = CsGeo<D>;
   constexpr int NC = G::NC;
   constexpr int QRB = G::QRB;
-  __shared__ __attribute__((aligned(1024))) char sQ[kCsHalves * kCsSlots * G::QBYTES];
+  constexpr int kThreads = HALVES * kCsWavesPerHalf * 64;
+  __shared__ __attribute__((aligned(1024))) char sQ[HALVES * kCsSlots * G::QBYTES];
   __shared__ __attribute__((aligned(16))) float sLse[kCsLseRows];
-  __shared__ double sAcc[kCsWavesPerHalf * KB * 64];
+  __shared__ double sAcc[HALVES == 2 ? kCsWavesPerHalf * KB * 64 : 1];   // second half's totals
   constexpr int kKeys = kCsWavesPerHalf * 32 * KB;   // keys per workgroup
 
   const int tid = threadIdx.x;
@@ -385,19 +390,19 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   for (int rb = r_begin; rb < r_end; rb += kCsLseRows) {
     const int nrows = min(kCsLseRows, r_end - rb);
     const int nch = ceil_div(nrows, kCsRows);
-    const int nj = ceil_div(nch, kCsHalves);   // chunks per half (the last may be empty)
+    const int nj = ceil_div(nch, HALVES);   // chunks per half (the last may be empty)
     __syncthreads();                           // previous pass done with sLse
-    // Q tiles of this half's first chunks (chunk c = 2j + half) ...
+    // Q tiles of this half's first chunks (chunk c = HALVES * j + half) ...
 #pragma unroll
     for (int j = 0; j < kCsSlots - 1; ++j) {
-      const int c = kCsHalves * j + half;
+      const int c = HALVES * j + half;
       cs_issue<D>(a, rs_q, sr.ntok, g, c < nch ? rb + c * kCsRows : R, R, myq + j * G::QBYTES, w4, lane);
     }
     // ... while the row LSEs are combined from the chunk partials:
     // lse = M + log2(sum_k l_k 2^(m_k - M)) (or the query partial's LSE in
     // log2 units); rows past r_end get +inf (weight 0).
     // All of a row's partials are loaded at once (KC <= kMaxKeyChunks).
-    for (int i = tid; i < nch * kCsRows; i += kCsThreads) {
+    for (int i = tid; i < nch * kCsRows; i += kThreads) {
       const int rr = rb + i;
       float lse = INFINITY;
       if (!CTX && a.score_from_partials) {
@@ -427,11 +432,11 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
       __syncthreads();       // ... everyone's, and the LSE table; slot of j-1 is free
       {
         const int jn = j + kCsSlots - 1;
-        const int cn = kCsHalves * jn + half;
+        const int cn = HALVES * jn + half;
         cs_issue<D>(a, rs_q, sr.ntok, g, (jn < nj && cn < nch) ? rb + cn * kCsRows : R, R,
                     myq + (jn % kCsSlots) * G::QBYTES, w4, lane);
       }
-      const int c = kCsHalves * j + half;
+      const int c = HALVES * j + half;
       if (c >= nch) continue;
       // Context selector: the chunk's tokens t see keys j <= t only.  A
       // split lies within one head, so the chunk's tokens are t_first + m
@@ -477,23 +482,29 @@ __global__ __launch_bounds__(kCsThreads, 1) void colsum_kernel(AttnArgs a, int K
   }
 
   // Column totals: the lane pair (l, l^32) holds the two row halves of a
-  // key's accumulator rows; the second workgroup half's totals are added to
+  // key's accumulator rows; a second workgroup half's totals are added to
   // the first's in a fixed order.
   double tot[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) tot[kb] = acc[kb] + __shfl_xor(acc[kb], 32);
-  __syncthreads();
-  if (half == 1) {
+  if (HALVES == 2) {
+    __syncthreads();
+    if (half == 1) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sAcc[(w4 * KB + kb) * 64 + lane] = tot[kb];
+      for (int kb = 0; kb < KB; ++kb) sAcc[(w4 * KB + kb) * 64 + lane] = tot[kb];
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) tot[kb] += sAcc[(w4 * KB + kb) * 64 + lane];
+    }
   }
-  __syncthreads();
   if (half == 0 && hi == 0) {
     float* out = gridDim.z == 1 ? scores + (long)hg * a.L : cpart + ((long)blockIdx.z * VH + hg) * a.L;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int j = key0 + 32 * kb + col;
-      if (j < a.L) out[j] = (float)(tot[kb] + sAcc[(w4 * KB + kb) * 64 + lane]);
+      if (j < a.L) out[j] = (float)tot[kb];
     }
   }
 }
@@ -549,15 +560,16 @@ size_t part_bytes(const AttnArgs& a) {
 
 }  // namespace
 
-template <bool CTX, int KB>
+template <bool CTX, int KB, int HALVES>
 void launch_colsum(const AttnArgs& a, int KC, const float2* part, float* scores, float* cpart, const ColSplits& cs,
                    hipStream_t s) {
   const dim3 grid(ceil_div(a.L, kCsWavesPerHalf * 32 * KB), a.V * a.Hkv, cs.total);
+  const dim3 block(HALVES * kCsWavesPerHalf * 64);
   if (a.D == 128)
-    hipLaunchKernelGGL((colsum_kernel<128, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+    hipLaunchKernelGGL((colsum_kernel<128, CTX, KB, HALVES>), grid, block, 0, s, a, KC, part, scores, cpart,
                        cs.per_head, cs.rows);
   else
-    hipLaunchKernelGGL((colsum_kernel<64, CTX, KB>), grid, dim3(kCsThreads), 0, s, a, KC, part, scores, cpart,
+    hipLaunchKernelGGL((colsum_kernel<64, CTX, KB, HALVES>), grid, block, 0, s, a, KC, part, scores, cpart,
                        cs.per_head, cs.rows);
 }
 
@@ -581,14 +593,17 @@ hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hi
     if (e != hipSuccess) return e;
   }
   const ColSplits cs = col_splits(a);
-  // More keys per wave read each Q fragment into more MFMAs (less LDS
-  // traffic per flop) but give fewer workgroups: the query rows take 96 keys
-  // per wave only when that still leaves a few workgroups per CU.
-  const bool wide = CTX || ceil_div(a.L, kCsWavesPerHalf * 32 * kCsKbQueryWide) * VH * cs.total >= kCsWideGrid;
-  if (wide)
-    launch_colsum<CTX, CTX ? kCsKbCtx : kCsKbQueryWide>(a, KC, part, scores, cpart, cs, s);
-  else
-    launch_colsum<CTX, kCsKbQuery>(a, KC, part, scores, cpart, cs, s);
+  // The context selector's grid holds every head's token splits (thousands
+  // of workgroups at 32K tokens); the query rows take single-half workgroups
+  // when there are at least four per CU, else two halves.
+  if constexpr (CTX) {
+    launch_colsum<true, kCsKbCtx, 1>(a, KC, part, scores, cpart, cs, s);
+  } else {
+    if (ceil_div(a.L, kCsWavesPerHalf * 32 * kCsKbQuery) * VH * cs.total >= kCsSingleGrid)
+      launch_colsum<false, kCsKbQuery, 1>(a, KC, part, scores, cpart, cs, s);
+    else
+      launch_colsum<false, kCsKbQuery, 2>(a, KC, part, scores, cpart, cs, s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cs.total == 1) return e;
   const long n = (long)VH * a.L;
