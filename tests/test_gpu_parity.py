@@ -222,3 +222,32 @@ def test_selection_across_list_lengths(L, lp):
     err = np.abs(got - want) / np.maximum(np.abs(want), 1e-30)
     assert err.max() < 1e-5, f"scores rel err {err.max():.2e}"
     check_idx(want, idx.cpu().numpy(), O.select_passing(want, lp), lp)
+
+
+@pytest.mark.parametrize("d,L", [(64, 1000), (128, 777)])
+def test_column_sums_on_a_large_grid(d, L):
+    # V * Hkv * ceil(L / 256) >= 1024 column-sum workgroups: the form with
+    # one 4-wave group per workgroup (three to a CU), here with a ragged last
+    # group of keys. Every score and index against the oracle, from the
+    # one-pass scoring and from the query partials' LSEs.
+    w = W.small_workload("bf16", Hq=8, Hkv=8, d=d, la=0, V=32, L=L, n_q=5, lp=100, seed=37)
+    assert w.n_hosts * w.n_kv_heads * math.ceil(L / 256) >= 1024
+    x = W.make_inputs(w)
+    plan = S.plan_for(w)
+    q, k, v = dev_inputs(x, w)
+    b = S.alloc_buffers(plan, q.device)
+    want = O.block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
+    sel = O.select_passing(want, w.lp)
+    S.spava_score_topk(plan, q, k, b.scores, b.idx, b.ws_score)
+    torch.cuda.synchronize()
+    err = np.abs(np64(b.scores) - want) / np.maximum(np.abs(want), 1e-30)
+    assert err.max() < 1e-5, f"one-pass scores rel err {err.max():.2e}"
+    check_idx(want, b.idx.cpu().numpy(), sel, w.lp)
+    S.spava_attn_fwd_phase(plan, S.SPAVA_PHASE_LOCAL, q, k, v, b.kp, b.vp, b.o, b.lse, b.o_part, b.lse_part)
+    scores = torch.zeros_like(b.scores)
+    idx = torch.zeros_like(b.idx)
+    S.spava_score_topk_from_partials(plan, q, k, b.lse_part, scores, idx)
+    torch.cuda.synchronize()
+    err = np.abs(np64(scores) - want) / np.maximum(np.abs(want), 1e-30)
+    assert err.max() < 1e-5, f"from-partials scores rel err {err.max():.2e}"
+    check_idx(want, idx.cpu().numpy(), sel, w.lp)
