@@ -20,7 +20,9 @@ from dataclasses import dataclass
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspava.so")
+# SPAVA_LIBRARY names another build of the same library to load instead of
+# the in-tree one (the host-sanitizer build of the CPU tests).
+LIB_PATH = os.environ.get("SPAVA_LIBRARY") or os.path.join(HERE, "libspava.so")
 
 SPAVA_OK, SPAVA_EINVAL, SPAVA_EUNSUPPORTED, SPAVA_EWORKSPACE, SPAVA_ELAUNCH = range(5)
 SPAVA_BF16, SPAVA_F32 = 0, 1

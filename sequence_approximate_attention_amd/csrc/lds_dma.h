@@ -51,7 +51,10 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
 // assembly so that the compiler keeps no wait bookkeeping of its own for these
 // copies: their completion is awaited explicitly (wait_vm) before the barrier
 // that publishes a ring slot.  M0 carries the LDS address; it needs one wait
-// state before the load.
+// state before the load.  The compiler does not accept M0 (a reserved
+// register) as a clobber, so it cannot be told that this statement writes
+// it: no other code in the kernels that use this copy may rely on M0, which
+// tests/test_device_asm.py checks in their generated assembly.
 __device__ __forceinline__ void copy16_to_lds(const u32x4& rsrc, unsigned soff, unsigned voff,
                                               unsigned lds) {
   asm volatile(
@@ -60,7 +63,7 @@ __device__ __forceinline__ void copy16_to_lds(const u32x4& rsrc, unsigned soff, 
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-      : "memory", "m0");
+      : "memory");
 }
 
 }  // namespace spava
