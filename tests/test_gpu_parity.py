@@ -63,6 +63,9 @@ SMALL = [
     # d = 64 with walks of up to 27 key tiles (both V ring slots reused many
     # times, ragged run ends inside tiles)
     W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=300, V=3, L=1000, n_q=40, lp=200, seed=13),
+    # blocks of one and two tokens: every walk a single ragged tile
+    W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=7, V=6, L=1, n_q=3, lp=1, seed=14),
+    W.small_workload("bf16", Hq=6, Hkv=3, d=128, la=0, V=3, L=2, n_q=5, lp=1, seed=15),
 ]
 
 
