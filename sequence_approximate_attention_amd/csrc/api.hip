@@ -85,7 +85,7 @@ int check_plan(const spava_plan* p) {
   const int esz = p->dtype == SPAVA_F32 ? 4 : 2;
   const int64_t st[4] = {p->q_stride_tok, p->q_stride_head, p->kv_stride_tok, p->kv_stride_head};
   for (int i = 0; i < 4; ++i)
-    if (st[i] < 0 || (st[i] * esz) % 16 != 0)
+    if (st[i] < 0 || st[i] % (16 / esz) != 0)
       return fail(SPAVA_EINVAL, "strides must be >= 0 and multiples of %d elements", 16 / esz);
   const double q_st = p->q_stride_tok ? (double)p->q_stride_tok : (double)p->n_q_heads * p->head_dim;
   const double q_sh = p->q_stride_head ? (double)p->q_stride_head : (double)p->head_dim;

@@ -68,6 +68,16 @@ def plan(**kw):
     (dict(q_stride_head=1 << 26), S.SPAVA_OK),
     (dict(q_stride_head=1 << 31), S.SPAVA_EINVAL),
     (dict(kv_stride_tok=1 << 22), S.SPAVA_EINVAL),
+    # strides near the int64 range are rejected without overflowing
+    (dict(kv_stride_tok=1 << 62), S.SPAVA_EINVAL),
+    (dict(q_stride_head=(1 << 63) - 1), S.SPAVA_EINVAL),
+    (dict(dtype=S.SPAVA_BF16, q_stride_tok=(1 << 62) + 8), S.SPAVA_EINVAL),
+    # sizes at the int32 limit are rejected without overflowing
+    (dict(n_hosts=(1 << 31) - 1, host_len=(1 << 31) - 1, lp=0), S.SPAVA_EINVAL),
+    (dict(n_anchor=(1 << 31) - 1), S.SPAVA_EINVAL),
+    (dict(n_query=(1 << 31) - 1), S.SPAVA_EINVAL),
+    (dict(n_q_heads=(1 << 31) - 1, n_kv_heads=1), S.SPAVA_EINVAL),
+    (dict(host_len=(1 << 31) - 1, lp=(1 << 31) - 1, n_hosts=1), S.SPAVA_EINVAL),
     # a token stride shorter than a row would overlap the next token's row
     (dict(kv_stride_tok=32, kv_stride_head=64), S.SPAVA_EINVAL),
     (dict(q_stride_tok=48), S.SPAVA_EINVAL),
@@ -110,6 +120,11 @@ def test_workspace_sizes():
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32)) == 4 * 1 * 128 * 2 * 4 + sc(128)
     assert S.spava_score_topk_context_ws_bytes(plan(dtype=S.SPAVA_F32, n_query=0)) == 4 * 1 * 128 * 2 * 4 + sc(128)
     assert S.spava_score_topk_context_ws_bytes(plan(lp=999)) == 0
+    # plans at the int32 limits: no size, no overflow
+    for kw in (dict(n_hosts=(1 << 31) - 1, host_len=(1 << 31) - 1, lp=0), dict(n_query=(1 << 31) - 1),
+               dict(n_q_heads=(1 << 31) - 1, n_kv_heads=1)):
+        assert S.spava_score_topk_ws_bytes(plan(**kw)) == 0
+        assert S.spava_score_topk_context_ws_bytes(plan(**kw)) == 0
 
 
 def test_null_and_misaligned_pointers_rejected_on_host():

@@ -54,7 +54,9 @@ def test_sanitizer_reports_planted_overflow(tmp_path):
 
 
 def test_abi_checks_are_clean_under_host_sanitizers(sanitized_lib):
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+    # -s: a sanitizer report goes to stderr just before the abort, which
+    # pytest's own capture would lose.
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_abi.py")],
                        env=sanitized_env(sanitized_lib), cwd=ROOT, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
