@@ -205,3 +205,45 @@ def test_noalloc_scoring_rejects_plans_beyond_its_scratch_on_the_host():
     # Argument checks as spava_score_topk: NULL idx with lp > 0.
     rc = S.lib().spava_score_topk_noalloc(ctypes.byref(fits.c()), fake, fake, fake, None, None)
     assert rc == S.SPAVA_EINVAL
+
+
+def _int32s():
+    from hypothesis import strategies as st
+    edge = st.sampled_from([-(1 << 31), -1, 0, 1, 2, 7, 64, 128, 1000, (1 << 15), (1 << 24), (1 << 31) - 1])
+    return st.one_of(edge, st.integers(-(1 << 31), (1 << 31) - 1), st.integers(0, 5000))
+
+
+def _int64s():
+    from hypothesis import strategies as st
+    edge = st.sampled_from([0, 8, 64, 128, 136, 1 << 22, 1 << 31, 1 << 62, (1 << 63) - 1, -8, -(1 << 63)])
+    return st.one_of(edge, st.integers(-(1 << 63), (1 << 63) - 1), st.integers(0, 1 << 20))
+
+
+def test_plan_arithmetic_never_misbehaves():
+    # Random plans, extreme values included: the check returns one of its
+    # codes, the workspace sizes are 0 exactly for rejected plans, and both
+    # are repeatable.  (The host-sanitizer run of this file turns any
+    # overflow or out-of-bounds access on the way into an abort.)
+    from hypothesis import given, settings, HealthCheck
+    from hypothesis import strategies as st
+
+    fields = st.fixed_dictionaries(dict(
+        n_anchor=_int32s(), n_hosts=_int32s(), host_len=_int32s(), n_query=_int32s(),
+        n_q_heads=_int32s(), n_kv_heads=_int32s(), head_dim=st.sampled_from([64, 128, 0, 96, -64]),
+        lp=_int32s(), dtype=st.sampled_from([S.SPAVA_BF16, S.SPAVA_F32, 2, -1]),
+        scale=st.sampled_from([0.0, 0.125, -1.0, float("inf"), float("nan"), 1e30]),
+        q_stride_tok=_int64s(), q_stride_head=_int64s(), kv_stride_tok=_int64s(), kv_stride_head=_int64s()))
+
+    @settings(max_examples=400, deadline=None, suppress_health_check=list(HealthCheck), derandomize=True)
+    @given(fields)
+    def run(kw):
+        p = S.Plan(**kw)
+        rc = S.spava_plan_check(p)
+        assert rc in (S.SPAVA_OK, S.SPAVA_EINVAL, S.SPAVA_EUNSUPPORTED)
+        assert S.spava_plan_check(p) == rc
+        for f in (S.spava_score_topk_ws_bytes, S.spava_score_topk_context_ws_bytes):
+            n = f(p)
+            assert (n == 0) == (rc != S.SPAVA_OK)
+            assert n % 256 == 0 and n == f(p)
+
+    run()
