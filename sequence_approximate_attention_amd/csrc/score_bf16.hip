@@ -575,8 +575,10 @@ void launch_colsum(const AttnArgs& a, int KC, const float2* part, float* scores,
 
 template <bool CTX>
 hipError_t launch_score_bf16_mode(const AttnArgs& a, void* ws, float* scores, hipStream_t s) {
+  // Scoring from the query partials passes no workspace: it reads no chunk
+  // partials and its single row split writes the scores directly.
   float2* part = (float2*)ws;
-  float* cpart = (float*)((char*)ws + part_bytes(a));
+  float* cpart = ws ? (float*)((char*)ws + part_bytes(a)) : nullptr;
   const int R = score_rows(a, 0).R;
   const int VH = a.V * a.Hkv;
   const int KC = key_chunks(a);

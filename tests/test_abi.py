@@ -247,3 +247,53 @@ def test_plan_arithmetic_never_misbehaves():
             assert n % 256 == 0 and n == f(p)
 
     run()
+
+
+@pytest.mark.parametrize("kw", [
+    None,   # every workload of the recipe
+    dict(n_anchor=0, n_hosts=1, host_len=(1 << 23) - 64, n_query=64, n_q_heads=1, n_kv_heads=1,
+         head_dim=128, lp=1024, dtype=S.SPAVA_BF16),
+    dict(n_anchor=100, n_hosts=65536, host_len=128, n_query=16, n_q_heads=2, n_kv_heads=1,
+         head_dim=64, lp=64, dtype=S.SPAVA_BF16),
+    dict(n_anchor=3, n_hosts=3, host_len=1, n_query=0, n_q_heads=8, n_kv_heads=8,
+         head_dim=128, lp=1, dtype=S.SPAVA_F32),
+], ids=["workloads", "one_long_block", "many_hosts", "tiny_f32_no_query"])
+def test_launch_setup_runs_to_the_launch_without_a_device(kw):
+    # Valid plans pass every host check and reach the kernel launches, which
+    # fail cleanly (SPAVA_ELAUNCH) where there is no GPU: the launch set-up
+    # (unit counts, splits, grids, workspace carving) runs on the host, and
+    # under the host-sanitizer build of this file any overflow in it aborts.
+    # The pointers are fake, so this runs only without a GPU.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer launch set-up runs on machines without a GPU")
+    import workloads as W
+    plans = [S.plan_for(w) for w in W.WORKLOADS + W.PAGE_DEFAULT_WORKLOADS] if kw is None else [plan(**kw)]
+    lib = S.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    for pl in plans:
+        assert S.spava_plan_check(pl) == S.SPAVA_OK
+        p = pl.c()
+        need = lib.spava_score_topk_ws_bytes(ctypes.byref(p))
+        need_ctx = lib.spava_score_topk_context_ws_bytes(ctypes.byref(p))
+        rcs = [lib.spava_score_topk(ctypes.byref(p), fake, fake, fake, fake, fake, need, None),
+               lib.spava_score_topk(ctypes.byref(p), fake, fake, None, fake, fake, need, None),
+               lib.spava_score_topk_context(ctypes.byref(p), fake, fake, fake, fake, fake, need_ctx, None),
+               lib.spava_gather_passing(ctypes.byref(p), fake, fake, fake, fake, fake, None),
+               lib.spava_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, None)]
+        if pl.n_query > 0:
+            rcs.append(lib.spava_score_topk_from_partials(ctypes.byref(p), fake, fake, fake, fake, fake, None))
+        if need <= S.SPAVA_NOALLOC_SCRATCH_BYTES:
+            rcs.append(lib.spava_score_topk_noalloc(ctypes.byref(p), fake, fake, fake, fake, None))
+        expect = [S.SPAVA_ELAUNCH] * len(rcs)
+        if pl.lp == 0:
+            expect[3] = S.SPAVA_OK   # nothing to gather
+        for ph in (S.SPAVA_PHASE_ALL, S.SPAVA_PHASE_LOCAL, S.SPAVA_PHASE_PASSING):
+            rcs.append(lib.spava_attn_fwd_phase(ctypes.byref(p), ph, fake, fake, fake, fake, fake, fake, fake,
+                                                fake, fake, None))
+            # one host: the PASSING phase has no rows to run
+            expect.append(S.SPAVA_OK if ph == S.SPAVA_PHASE_PASSING and pl.n_hosts == 1 else S.SPAVA_ELAUNCH)
+        assert rcs == expect, (pl, rcs, lib.spava_last_error())
+    assert lib.spava_lse_merge(33, 512, 28, 128, fake, fake, fake, 28 * 128, fake, 512, S.SPAVA_BF16,
+                               None) == S.SPAVA_ELAUNCH
+    assert lib.spava_kv_overlap(128, 4096, fake, fake, fake, None) == S.SPAVA_ELAUNCH
