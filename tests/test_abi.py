@@ -297,3 +297,31 @@ def test_launch_setup_runs_to_the_launch_without_a_device(kw):
     assert lib.spava_lse_merge(33, 512, 28, 128, fake, fake, fake, 28 * 128, fake, 512, S.SPAVA_BF16,
                                None) == S.SPAVA_ELAUNCH
     assert lib.spava_kv_overlap(128, 4096, fake, fake, fake, None) == S.SPAVA_ELAUNCH
+
+
+def test_last_error_is_per_thread():
+    # The error text is thread-local: threads that fail different checks at
+    # the same time each read back their own message (ctypes releases the
+    # GIL during the calls, so the threads do overlap in the library).
+    import threading
+    lib = S.lib()
+    cases = {"lp": (plan(lp=129), b"lp (129)"), "dtype": (plan(dtype=7), b"dtype 7"),
+             "heads": (plan(n_q_heads=3, n_kv_heads=2), b"n_q_heads (3)"), "ok": (plan(), b"")}
+    bad = []
+
+    def worker(name):
+        p, want = cases[name]
+        pc = p.c()
+        for _ in range(2000):
+            lib.spava_plan_check(ctypes.byref(pc))
+            got = lib.spava_last_error()
+            if (want and want not in got) or (not want and got):
+                bad.append((name, got))
+                return
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in cases for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:4]
