@@ -255,3 +255,14 @@ def test_walk_catches_a_cursor_that_runs_past_the_walk(w):
     assert (w.n_tokens * w.n_kv_heads * w.head_dim * 2) % (2 << 20) == 0
     with pytest.raises(AssertionError, match="outside"):
         attention_copies(w, w.head_dim, past_walk="advance")
+
+
+RANDOM_BF16 = [w for w in W.random_small_workloads() if w.dtype == W.BF16]
+
+
+@pytest.mark.parametrize("w", RANDOM_BF16, ids=lambda w: w.name)
+def test_random_shapes_copies_in_bounds(w):
+    # The seeded random shapes of the GPU parity sweep, before any GPU runs them.
+    assert attention_copies(w, w.head_dim) > 0
+    assert score_copies(w, w.head_dim) > 0 or w.n_query == 0
+    assert score_copies(w, w.head_dim, ctx=True) > 0

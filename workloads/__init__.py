@@ -192,3 +192,27 @@ def small_workload(dtype=BF16, *, Hq=4, Hkv=2, d=128, la=48, V=3, L=100, n_q=20,
     """A small ragged workload (sizes not multiples of the kernels' tiles)."""
     return Workload(f"small_{dtype}_{Hq}x{Hkv}x{d}_la{la}_V{V}_L{L}_q{n_q}_lp{lp}", dtype,
                     Hq, Hkv, d, la, V, L, n_q, lp, structure, arg, seed=seed)
+
+
+def random_small_workloads(count: int = 120, seed: int = 2026) -> list[Workload]:
+    """A fixed, seeded list of small ragged shapes drawn at random (head
+    grouping, width, anchor, hosts, block length, query length, passing
+    length with extra weight on 0, 1 and L; a few float32), sized so that the
+    oracle finishes each in well under a second."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 7]))
+        while Hkv * G > 16:
+            G = int(rng.choice([1, 2, 3]))
+        d = int(rng.choice([64, 128]))
+        la = int(rng.choice([0, int(rng.integers(1, 300))]))
+        V = int(rng.integers(1, 7))
+        L = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 700))]))
+        n_q = int(rng.choice([0, int(rng.integers(1, 49))]))
+        lp = int(rng.choice([0, 1, L, int(rng.integers(0, L + 1))]))
+        dtype = F32 if rng.random() < 0.15 else BF16
+        out.append(small_workload(dtype, Hq=Hkv * G, Hkv=Hkv, d=d, la=la, V=V, L=L, n_q=n_q, lp=lp,
+                                  seed=1000 + i))
+    return out
