@@ -13,7 +13,8 @@
 //
 // Iteration i (one workgroup barrier each):
 //   softmax wave:  S(i) = K(i) Q^T || P(i-1) = exp2(S(i-1) - m), written to
-//                  LDS with its rescale factor; row maxima of S(i)
+//                  LDS with its rescale factor; row maxima of S(i); then the
+//                  first fragments of K(i+1), complete since the barrier
 //   output wave:   copies of V(i-1) and K(i+2); O = O*alpha(i-2) + V(i-2) P(i-2)
 // LDS: a 2-slot V ring at address 0 (so every V read is a lane offset plus an
 // immediate), a 3-slot K ring (both filled by buffer_load_dwordx4 ... lds
@@ -416,8 +417,17 @@ __device__ __forceinline__ bool soft_probs(const Scores& sp, char* pwrite, const
 // HEAD = 1 is iteration 0: there is no P(-1), only S(0) is computed.  HEAD = 2
 // is iteration 1: no row has a reference yet, so P(0) is computed once,
 // against S(0)'s own row maxima, instead of speculatively and again.
+// ring carries the first K fragments from one iteration to the next: K(i+1)
+// is complete from the barrier of iteration i on (the output waves wait for
+// all of their copies before it), so iteration i reads K(i+1)'s first
+// fragments after its own MFMAs, and iteration i+1's first MFMAs need not
+// wait for LDS after its barrier.  Iteration 0 reads its own.
+struct KSlots {
+  const char* cur;   // K(i)
+  const char* nxt;   // K(i+1)
+};
 template <int D, bool MASK, bool LIVE = true, int HEAD = 0>
-__device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __restrict__ kread,
+__device__ __forceinline__ void soft_iter(int i, const Runs& run, KSlots ks, bf16x8 (&ring)[4],
                                           char* __restrict__ pwrite, float* __restrict__ awrite,
                                           int* __restrict__ fwrite, const SoftCtx<D>& cx, SoftState& st,
                                           const Scores& s_prev, Scores& s_new) {
@@ -430,6 +440,7 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   __syncthreads();
   // Fragment n = (d chunk c, key half h2) with h2 fastest: the four
   // accumulators (qb, h2) alternate, so no MFMA waits on the one before.
+  const char* const kread = ks.cur;
   auto kfrag = [&](int n) {
     return *(const bf16x8*)(kread + cx.koff[n / 2] + (n % 2) * 32 * KRB);
   };
@@ -444,8 +455,7 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
   for (int qb = 0; qb < 2; ++qb) mu[qb] = (st.m[qb] == -INFINITY) ? 0.0f : st.m[qb];
   float acc[2] = {0.0f, 0.0f};
   bf16x8 pb;
-  bf16x8 ring[RING];
-  if (LIVE) {
+  if (LIVE && HEAD == 1) {
 #pragma unroll
     for (int n = 0; n < RING; ++n) ring[n] = kfrag(n);
   }
@@ -471,6 +481,10 @@ __device__ __forceinline__ void soft_iter(int i, const Runs& run, const char* __
         if (e == 7) *(bf16x8*)(pwrite + p_off(qb, kc, cx.lane)) = pb;
       }
     }
+  }
+  if (LIVE) {   // K(i+1)'s first fragments for the next iteration
+#pragma unroll
+    for (int n = 0; n < RING; ++n) ring[n] = *(const bf16x8*)(ks.nxt + cx.koff[n / 2] + (n % 2) * 32 * KRB);
   }
   if (HEAD != 1) {
     bool grow = HEAD == 2;
@@ -580,8 +594,9 @@ __device__ __forceinline__ void v_read_offsets(int lane, int (&voff)[2][D / 32])
 
 // One output-wave iteration: copies of V(i-1) (to vload; empty for i = 0)
 // and K(i+2) (to kload), then O = O * alpha(i-2) + V(i-2) P(i-2) from vread,
-// pread, aread, fread.  Once only the last K copies (K(i+1)) may still be in
-// flight, V(i-2) and K(i) have landed; the barrier publishes them.
+// pread, aread, fread.  Once all of this wave's copies have landed (V(i-2),
+// K(i) and K(i+1), issued an iteration or more ago), the barrier publishes
+// them: the softmax waves read K(i+1)'s first fragments before the next one.
 template <int D>
 __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __restrict__ vread,
                                          const char* __restrict__ pread, const float* __restrict__ aread,
@@ -591,7 +606,7 @@ __device__ __forceinline__ void out_iter(int i, const Runs& run, const char* __r
   using G = Geo<D>;
   constexpr int NDB = G::NDB;
   asm volatile("" : "+s"(i));
-  wait_vm<G::KINST>();
+  wait_vm<0>();
   __syncthreads();
   constexpr int NB = 4 * NDB;   // V^T fragments (16-key chunk, 32-channel block)
   constexpr int RING = 4;
@@ -790,9 +805,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     // Slots of iteration i: K(i) in i % 3; P(i-1) and its factor in buffer
     // (i-1) % 2 (even and odd iterations are unrolled with fixed buffers).
     int k3 = 0;   // i % 3
+    bf16x8 kring[4];
     auto knext = [&]() {
-      const char* r = sK + k3 * G::KBYTES;
+      KSlots r;
+      r.cur = sK + k3 * G::KBYTES;
       k3 = (k3 == kKSlots - 1) ? 0 : k3 + 1;
+      r.nxt = sK + k3 * G::KBYTES;
       return r;
     };
     char* const p0 = sP + pair * kPBytes;
@@ -805,32 +823,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     // Iterations 0 and 1: S(0) alone, then S(1) with P(0) against S(0)'s
     // maxima (a walk of one tile makes iteration 1 its last, dead one).
     if (n_plain >= 2) {
-      soft_iter<D, false, true, 1>(0, run, knext(), p1, a1, f1, cx, st, sA, sB);
-      soft_iter<D, false, true, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+      soft_iter<D, false, true, 1>(0, run, knext(), kring, p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, false, true, 2>(1, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
     } else {
-      soft_iter<D, true, true, 1>(0, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, true, true, 1>(0, run, knext(), kring, p1, a1, f1, cx, st, sA, sB);
       if (run.T >= 2)
-        soft_iter<D, true, true, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+        soft_iter<D, true, true, 2>(1, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
       else
-        soft_iter<D, true, false, 2>(1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+        soft_iter<D, true, false, 2>(1, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
     }
     for (int i = 2; i < n_plain; i += 2) {
-      soft_iter<D, false>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
-      soft_iter<D, false>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+      soft_iter<D, false>(i, run, knext(), kring, p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, false>(i + 1, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
     }
     for (int i = max(2, n_plain); i < run.T; i += 2) {
-      soft_iter<D, true>(i, run, knext(), p1, a1, f1, cx, st, sA, sB);
+      soft_iter<D, true>(i, run, knext(), kring, p1, a1, f1, cx, st, sA, sB);
       if (i + 1 >= run.T) break;
-      soft_iter<D, true>(i + 1, run, knext(), p0, a0, f0, cx, st, sB, sA);
+      soft_iter<D, true>(i + 1, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
     }
     // Iteration T computes P(T-1) only; in iteration T+1 (the output wave's
     // last P V) this wave has nothing left that is read, so it only meets the
     // barrier.
     if (run.T >= 2) {
       if ((run.T & 1) == 0)
-        soft_iter<D, true, false>(run.T, run, knext(), p1, a1, f1, cx, st, sA, sB);
+        soft_iter<D, true, false>(run.T, run, knext(), kring, p1, a1, f1, cx, st, sA, sB);
       else
-        soft_iter<D, true, false>(run.T, run, knext(), p0, a0, f0, cx, st, sB, sA);
+        soft_iter<D, true, false>(run.T, run, knext(), kring, p0, a0, f0, cx, st, sB, sA);
     }
     __syncthreads();
     // Row sums to the output wave; LSE out.
