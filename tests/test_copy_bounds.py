@@ -260,9 +260,16 @@ def test_walk_catches_a_cursor_that_runs_past_the_walk(w):
 RANDOM_BF16 = [w for w in W.random_small_workloads() if w.dtype == W.BF16]
 
 
+RANDOM_ALL = W.random_small_workloads()
+
+
 @pytest.mark.parametrize("w", RANDOM_BF16, ids=lambda w: w.name)
 def test_random_shapes_copies_in_bounds(w):
-    # The seeded random shapes of the GPU parity sweep, before any GPU runs them.
-    assert attention_copies(w, w.head_dim) > 0
-    assert score_copies(w, w.head_dim) > 0 or w.n_query == 0
-    assert score_copies(w, w.head_dim, ctx=True) > 0
+    # The seeded random shapes of the GPU parity sweep, before any GPU runs
+    # them, in the layout the sweep also gives them (dense for all; packed
+    # QKV or head-major for shape index 1 or 2 modulo 3).
+    layouts = [None, [None, "packed", "heads_major"][RANDOM_ALL.index(w) % 3]]
+    for strides in dict.fromkeys(layouts):
+        assert attention_copies(w, w.head_dim, strides=strides) > 0
+        assert score_copies(w, w.head_dim, strides=strides) > 0 or w.n_query == 0
+        assert score_copies(w, w.head_dim, ctx=True, strides=strides) > 0
