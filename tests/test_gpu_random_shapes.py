@@ -110,3 +110,62 @@ def test_random_shape(w):
         if w.dtype == W.BF16:
             s2, i2 = context(ps, qs, ks)
             assert torch.equal(s2, scores) and torch.equal(i2, idx), f"{layout.__name__}: context selector"
+
+
+def merge_cases(count=40, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        P = int(rng.choice([1, 2, int(rng.integers(3, 12)), int(rng.integers(12, 41))]))
+        R = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(64, 300))]))
+        H = int(rng.integers(1, 17))
+        D = int(rng.choice([4, 8, 60, 64, 128, 132]))
+        bf16 = bool(rng.random() < 0.5)
+        pad_row = int(rng.choice([0, 0, 4, 36]))     # extra elements per output row
+        pad_lse = int(rng.choice([0, 0, 3, 50]))     # extra elements per LSE head row
+        out.append((i, P, R, H, D, bf16, pad_row, pad_lse))
+    return out
+
+
+@pytest.mark.parametrize("case", merge_cases(), ids=lambda c: "P{1}_R{2}_H{3}_D{4}_{5}_pad{6}_{7}".format(
+    *c[:5], "bf16" if c[5] else "f32", c[6], c[7]))
+def test_random_merge(case):
+    # spava_lse_merge on random partition counts, rows, heads, widths (any
+    # multiple of 4), output dtypes and output strides, with whole partials,
+    # single (row, head) entries and whole rows at LSE = -inf, and LSE
+    # spreads from 0 to 80 (weights far below float32's range).
+    i, P, R, H, D, bf16, pad_row, pad_lse = case
+    rng = np.random.default_rng(1000 + i)
+    o_part = rng.standard_normal((P, R, H, D)).astype(np.float32)
+    spread = float(rng.choice([0.0, 1.0, 5.0, 80.0]))
+    lse_part = (rng.standard_normal((P, H, R)) * spread + rng.standard_normal()).astype(np.float32)
+    lse_part[rng.random((P, H, R)) < 0.1] = -np.inf
+    if P > 1:
+        lse_part[int(rng.integers(P))] = -np.inf
+    lse_part[:, :, int(rng.integers(R))] = -np.inf
+    row_stride, head_stride = H * D + pad_row, R + pad_lse
+    dt = torch.bfloat16 if bf16 else torch.float32
+    o_full = torch.full((R, row_stride), float("nan"), dtype=dt, device="cuda")
+    lse_full = torch.full((H, head_stride), float("nan"), dtype=torch.float32, device="cuda")
+    S.spava_lse_merge(torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda(), o_full, row_stride,
+                      lse_full, head_stride)
+    torch.cuda.synchronize()
+    ro, rl = O.lse_merge(o_part, lse_part.transpose(0, 2, 1))
+    o = np64(o_full[:, :H * D].reshape(R, H, D))
+    lse = np64(lse_full[:, :R]).T
+    # O: the float32 merge, then (bf16 outputs) one round-to-nearest to 8
+    # significant bits, at most 2^-8 of the value; LSE: float32 of
+    # magnitude up to a few hundred here, so a relative bound.
+    rel_o = 2.0 ** -8 if bf16 else 2e-6
+    err_o = np.abs(o - ro) - (rel_o * np.abs(ro) + 1e-5)
+    assert err_o.max() <= 0, f"merge O off by {err_o.max():.3e} beyond the bound"
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), fin) and (lse[~fin] == -np.inf).all()
+    err_l = np.abs(lse[fin] - rl[fin]) - (2e-5 + 4e-7 * np.abs(rl[fin]))
+    assert err_l.size == 0 or err_l.max() <= 0, f"merge LSE off by {err_l.max():.3e} beyond the bound"
+    assert (o[~fin] == 0).all()
+    # the padding of the strided outputs is left alone
+    if pad_row:
+        assert torch.isnan(o_full[:, H * D:].float()).all()
+    if pad_lse:
+        assert torch.isnan(lse_full[:, R:]).all()
