@@ -167,6 +167,14 @@ def _expect(t, shape, dtype, name, strides=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _reach(t, n_elems, name):
+    """Raise unless the n_elems elements from t's first element lie inside its
+    storage (a strided output written through a plain pointer)."""
+    end = (t.storage_offset() + n_elems) * t.element_size()
+    if n_elems > 0 and end > t.untyped_storage().nbytes():
+        raise ValueError(f"{name}: {n_elems} elements from its first element run past the end of its storage")
+
+
 def spava_plan_check(plan: Plan) -> int:
     return lib().spava_plan_check(ctypes.byref(plan.c()))
 
@@ -285,6 +293,11 @@ def spava_lse_merge(o_part, lse_part, o, o_row_stride, lse, lse_head_stride, str
             raise ValueError(f"{n} must be a contiguous float32 device tensor")
     if o.dtype not in (torch.bfloat16, torch.float32) or lse.dtype != torch.float32:
         raise ValueError("o must be bf16/f32 and lse f32")
+    if not o.is_cuda or not lse.is_cuda:
+        raise ValueError("o and lse must be device tensors")
+    if R > 0:
+        _reach(o, (R - 1) * int(o_row_stride) + H * D, "o")
+        _reach(lse, (H - 1) * int(lse_head_stride) + R, "lse")
     out_dtype = SPAVA_BF16 if o.dtype == torch.bfloat16 else SPAVA_F32
     _check(lib().spava_lse_merge(P, R, H, D, _ptr(o_part), _ptr(lse_part), _ptr(o), int(o_row_stride),
                                  _ptr(lse), int(lse_head_stride), out_dtype, _stream(stream)))

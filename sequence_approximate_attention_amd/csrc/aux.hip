@@ -40,16 +40,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partial attention results (axiom on Eq. 5 / Appendix A
 // in the APB-V review: merging through the FlashAttention lse is exact).
-// One thread per (row, head, 4 channels).  The partials are taken in chunks
-// of at most kMergeChunk: every LSE and O load of a chunk is issued before
-// any of them is used, so a wave has a whole chunk of reads in flight at once
-// (one memory round trip per chunk), and the chunks are merged online: the
-// running maximum m, the weight sum and the weighted O are rescaled when a
-// chunk raises m.  The sums run in partial order, so the result is
+// One thread per (row, head, 4 channels); it walks the partials in order and
+// merges them online: the running maximum m, the weight sum and the weighted
+// O are rescaled when a partial raises m, so each weight is exp(lse - m) with
+// m the maximum so far.  The sums run in partial order, so the result is
 // deterministic.
+//
+// The loads of the next PF partials are in flight while one is merged.  The
+// partials of one (row, head) lie n_rows*n_heads*d*4 bytes apart (7 MiB at
+// the 256K frame shape), so every partial in flight is another far-apart
+// region per wave; a shallow ring (PF = 2) keeps the chip's reads in few
+// DRAM regions at a time and reads faster than issuing a dozen partials at
+// once (68 % against 59 % of HBM bandwidth at 33 partials).  Grids too small
+// to fill the chip twice over take a deeper ring (PF = 8) so that enough
+// bytes are in flight.
 // ---------------------------------------------------------------------------
-constexpr int kMergeChunk = 16;
-
+template <int PF>
 __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
                                                     const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part,
@@ -61,51 +67,46 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
   const long total = (long)R * H * cq;
   if (gid >= total) return;
   const int c4 = (int)(gid % cq);
-  const int a = (int)((gid / cq) % H);
-  const int r = (int)(gid / ((long)cq * H));
-  const float* lp_ra = lse_part + (long)a * R + r;                  // + p * H * R
-  const float* op_ra = o_part + ((long)r * H + a) * D + c4 * 4;      // + p * R * H * D
+  const long ra = gid / cq;               // r * H + a
+  const int a = (int)(ra % H);
+  const int r = (int)(ra / H);
+  const float* lp_ra = lse_part + (long)a * R + r;   // + p * H * R
+  const float* op_ra = o_part + ra * D + c4 * 4;     // + p * R * H * D
   const long lp_step = (long)H * R, op_step = (long)R * H * D;
-  // Chunks of equal size (the last one no longer than the others).
-  const int n_chunks = (P + kMergeChunk - 1) / kMergeChunk;
-  const int cs = (P + n_chunks - 1) / n_chunks;
+  float lb[PF];
+  float4 xb[PF];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    if (q < P) {
+      lb[q] = lp_ra[q * lp_step];
+      xb[q] = *(const float4*)(op_ra + q * op_step);
+    }
+  }
   float m = -INFINITY, wsum = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p0 = 0; p0 < P; p0 += cs) {
-    const int n = min(cs, P - p0);
-    float l[kMergeChunk];
-    float4 x[kMergeChunk];
+  for (int p0 = 0; p0 < P; p0 += PF) {
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
-      if (u < n) {
-        l[u] = lp_ra[(p0 + u) * lp_step];
-        x[u] = *(const float4*)(op_ra + (p0 + u) * op_step);
-      }
-    }
-    float mc = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u)
-      if (u < n) mc = fmaxf(mc, l[u]);
-    const float m_new = fmaxf(m, mc);
-    if (m_new == -INFINITY) continue;   // no finite partial yet
-    if (m_new != m) {                   // move the reference (0 * the empty start is 0)
-      const float sc = (m == -INFINITY) ? 0.0f : expf(m - m_new);
-      acc.x *= sc;
-      acc.y *= sc;
-      acc.z *= sc;
-      acc.w *= sc;
-      wsum *= sc;
+    for (int sl = 0; sl < PF; ++sl) {
+      const int p = p0 + sl;
+      if (p >= P) break;
+      const float l = lb[sl];
+      const float4 x = xb[sl];
+      // A partial with lse = -inf has weight 0 and its O is not read into
+      // the sums; while m is -inf (no finite partial yet) the sums are 0.
+      const bool up = l > m;
+      const float m_new = up ? l : m;
+      const float sc = up ? expf(m - l) : 1.0f;   // exp(-inf) = 0 for the first finite partial
+      const float w = (l == -INFINITY) ? 0.0f : expf(l - m_new);
+      acc.x = acc.x * sc + w * x.x;
+      acc.y = acc.y * sc + w * x.y;
+      acc.z = acc.z * sc + w * x.z;
+      acc.w = acc.w * sc + w * x.w;
+      wsum = wsum * sc + w;
       m = m_new;
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
-      if (u < n) {
-        const float w = expf(l[u] - m);
-        acc.x += w * x[u].x;
-        acc.y += w * x[u].y;
-        acc.z += w * x[u].z;
-        acc.w += w * x[u].w;
-        wsum += w;
+      const int pn = p + PF;
+      if (pn < P) {                       // refill the slot just merged
+        lb[sl] = lp_ra[pn * lp_step];
+        xb[sl] = *(const float4*)(op_ra + pn * op_step);
       }
     }
   }
@@ -128,6 +129,9 @@ __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
   if (c4 == 0) lse[(long)a * lse_head_stride + r] = (wsum > 0.0f) ? m + logf(wsum) : -INFINITY;
 }
 
+// Workgroups below which the merge takes the deeper load ring (two per CU).
+constexpr long kMergeDeepBelow = 512;
+
 }  // namespace
 
 hipError_t launch_gather(const void* k, const void* v, const int32_t* idx, void* kp, void* vp,
@@ -148,8 +152,12 @@ hipError_t launch_merge(int P, int R, int H, int D, const float* o_part, const f
   const long total = (long)R * H * (D / 4);
   if (total == 0) return hipSuccess;
   const long blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P, R, H, D, o_part,
-                     lse_part, o, o_row_stride, lse, lse_head_stride, out_bf16);
+  if (blocks < kMergeDeepBelow)
+    hipLaunchKernelGGL(merge_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, P, R, H, D, o_part,
+                       lse_part, o, o_row_stride, lse, lse_head_stride, out_bf16);
+  else
+    hipLaunchKernelGGL(merge_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, P, R, H, D, o_part,
+                       lse_part, o, o_row_stride, lse, lse_head_stride, out_bf16);
   return hipGetLastError();
 }
 

@@ -325,3 +325,26 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not bad, bad[:4]
+
+
+def test_binding_rejects_strided_outputs_past_their_storage():
+    # spava_lse_merge writes o and lse through plain pointers with the given
+    # strides; the binding checks that the last element written lies inside
+    # each tensor's storage (an output of the wrong dtype or too few rows is
+    # rejected before the call).
+    import torch
+    o = torch.empty(4 * 64 + 10, dtype=torch.bfloat16)
+    S._reach(o, 4 * 64 + 10, "o")
+    S._reach(o[10:], 4 * 64, "o")
+    S._reach(o, 0, "o")
+    with pytest.raises(ValueError, match="past the end"):
+        S._reach(o[10:], 4 * 64 + 1, "o")
+    # Element counts are in the tensor's own dtype: float32 needs twice the bytes.
+    f32 = torch.empty(4 * 64 + 10, dtype=torch.bfloat16).view(torch.float32)
+    S._reach(f32, (4 * 64 + 10) // 2, "o")
+    with pytest.raises(ValueError, match="past the end"):
+        S._reach(f32, (4 * 64 + 10) // 2 + 1, "o")
+    lse = torch.empty(3, 100)
+    S._reach(lse[:, 40:], 2 * 100 + 60, "lse")
+    with pytest.raises(ValueError, match="past the end"):
+        S._reach(lse[:, 40:], 2 * 100 + 61, "lse")
