@@ -106,49 +106,30 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; returns this thread's prefix and
-// writes the total to *total.
-__device__ int block_exclusive_scan(int x, int* sWave, int* total) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sWave[wave] = incl;
-  __syncthreads();
-  if (tid < 64) {
-    int w = (tid < kTopkThreads / 64) ? sWave[tid] : 0;
-    int wi = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(wi, o);
-      if (lane >= o) wi += y;
-    }
-    if (tid < kTopkThreads / 64) sWave[tid] = wi - w;   // exclusive wave offsets
-    if (tid == kTopkThreads / 64 - 1) sWave[kTopkThreads / 64] = wi;
-  }
-  __syncthreads();
-  const int res = sWave[wave] + incl - x;
-  *total = sWave[kTopkThreads / 64];
-  __syncthreads();
-  return res;
-}
-
 // Each thread owns the contiguous keys [j0, j1) of the list, so the kept
 // indices come out in index order.  With NPT > 0 (lists of at most
 // NPT * kTopkThreads keys) the thread reads its keys from memory once and
 // every pass below works on registers; NPT = 0 reads them again per pass.
+//
+// Radix select of the lp-th largest order key.  All keys lie between the
+// list's smallest and largest key, so they share those two keys' common
+// leading bits: the passes start below them, 8 bits at a time.  After each
+// pass's histogram every wave reads all 256 bins and finds the digit itself,
+// so a pass costs one barrier.  The emit takes one scan of two counts per
+// thread (keys above the threshold, keys equal to it): the equal keys kept
+// are the take_eq lowest-indexed ones, so a thread's first output position
+// is (keys above, before it) + min(equal keys before it, take_eq).
 template <int NPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
                                                             int32_t* __restrict__ idx, int L, int lp) {
-  __shared__ int sHist[256];
-  __shared__ int sWave[kTopkThreads / 64 + 1];
-  __shared__ int sSel[2];
+  constexpr int kWaves = kTopkThreads / 64;
+  constexpr int kPasses = 4;                 // 32 bits, 8 per pass
+  __shared__ int sHist[kPasses * 256];
+  __shared__ uint32_t sLo[kWaves], sHi[kWaves];
+  __shared__ int sGt[kWaves], sEq[kWaves];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const float* sc = scores + (long)blockIdx.x * L;
   int32_t* out = idx + (long)blockIdx.x * lp;
 
@@ -167,87 +148,128 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   auto key = [&](int e) -> uint32_t { return NPT > 0 ? cache[e] : order_key(sc[j0 + e]); };
   const int n_loop = NPT > 0 ? NPT : n;
 
-  // Radix select of the lp-th largest order key, 8 bits at a time.
-  uint32_t prefix = 0, pmask = 0;
-  int need = lp;  // rank still to find among keys matching prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) sHist[tid] = 0;
-    __syncthreads();
+  for (int i = tid; i < kPasses * 256; i += kTopkThreads) sHist[i] = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < n_loop; ++e) {
+    if (e >= n) break;
+    const uint32_t u = key(e);
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+  }
+  if (lane == 0) {
+    sLo[wave] = lo;
+    sHi[wave] = hi;
+  }
+  __syncthreads();
+  lo = sLo[0];
+  hi = sHi[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    lo = min(lo, sLo[w]);
+    hi = max(hi, sHi[w]);
+  }
+  // Bits at and above 'top' are decided: prefix holds them, pmask marks them.
+  int top = (lo == hi) ? 0 : 32 - __clz(lo ^ hi);
+  uint32_t pmask = top >= 32 ? 0u : ~((1u << top) - 1u);
+  uint32_t prefix = lo & pmask;
+  int need = lp;   // rank still to find among the keys that match prefix
+  for (int pass = 0; top > 0; ++pass) {
+    const int w = min(8, top);
+    const int shift = top - w;
+    const uint32_t dm = (1u << w) - 1u;
+    int* h = sHist + pass * 256;
 #pragma unroll
     for (int e = 0; e < n_loop; ++e) {
       if (e >= n) break;
       const uint32_t u = key(e);
-      if ((u & pmask) == prefix) atomicAdd(&sHist[(u >> shift) & 255], 1);
+      if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & dm], 1);
     }
     __syncthreads();
-    // Count of keys in digits above b (suffix sum from the top), by wave 0..3.
-    int cnt = 0, above = 0;
-    if (tid < 256) {
-      const int b = 255 - tid;           // tid 0 <-> digit 255
-      cnt = sHist[b];
-    }
-    // inclusive scan over tid (digits from the top) within the first 256 threads
-    int incl = cnt;
-    {
-      const int lane = tid & 63;
+    // Lane l holds bins 255-4l .. 252-4l (lane 0 the highest digits).
+    int c[4];
+    int sum = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+    for (int i = 0; i < 4; ++i) {
+      c[i] = h[255 - 4 * lane - i];
+      sum += c[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int above = incl - sum;   // keys in higher digits than this lane's bins
+    const bool mine = above < need && need <= incl;
+    int dsel = 0, nsel = 0;
+    if (mine) {
+      int a = above;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (a < need && need <= a + c[i]) {
+          dsel = 255 - 4 * lane - i;
+          nsel = need - a;
+        }
+        a += c[i];
       }
-      if (tid < 256 && lane == 63) sWave[tid >> 6] = incl;
-      __syncthreads();
-      int off = 0;
-      for (int w = 0; w < (tid >> 6) && w < 4; ++w) off += sWave[w];
-      incl += off;
-      above = incl - cnt;
     }
-    if (tid < 256 && above < need && need <= incl) {
-      sSel[0] = 255 - tid;
-      sSel[1] = need - above;
-    }
-    __syncthreads();
-    const uint32_t digit = (uint32_t)sSel[0];
-    need = sSel[1];
-    prefix |= digit << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
+    const unsigned long long bal = __ballot(mine);
+    const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+    dsel = __shfl(dsel, src);
+    nsel = __shfl(nsel, src);
+    prefix |= ((uint32_t)dsel & dm) << shift;
+    pmask |= dm << shift;
+    need = nsel;
+    top = shift;
   }
   const uint32_t thr = prefix;  // order key of the lp-th largest score
   const int take_eq = need;     // keys equal to thr that are kept (lowest indices)
 
-  int n_eq = 0;
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < n_loop; ++e) {
     if (e >= n) break;
-    n_eq += (key(e) == thr);
+    const uint32_t u = key(e);
+    n_gt += (u > thr);
+    n_eq += (u == thr);
   }
-  int eq_total;
-  int eq_before = block_exclusive_scan(n_eq, sWave, &eq_total);
-  int n_sel = 0;
-  {
-    int q = eq_before;
+  int ig = n_gt, ie = n_eq;
 #pragma unroll
-    for (int e = 0; e < n_loop; ++e) {
-      if (e >= n) break;
-      const uint32_t u = key(e);
-      if (u > thr) ++n_sel;
-      else if (u == thr) { if (q < take_eq) ++n_sel; ++q; }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yg = __shfl_up(ig, o);
+    const int ye = __shfl_up(ie, o);
+    if (lane >= o) {
+      ig += yg;
+      ie += ye;
     }
   }
-  int sel_total;
-  int pos = block_exclusive_scan(n_sel, sWave, &sel_total);
-  {
-    int q = eq_before;
+  if (lane == 63) {
+    sGt[wave] = ig;
+    sEq[wave] = ie;
+  }
+  __syncthreads();
+  int og = 0, oe = 0;
+  for (int w = 0; w < wave; ++w) {
+    og += sGt[w];
+    oe += sEq[w];
+  }
+  const int eq_before = oe + ie - n_eq;
+  int pos = og + ig - n_gt + min(eq_before, take_eq);
+  int q = eq_before;
 #pragma unroll
-    for (int e = 0; e < n_loop; ++e) {
-      if (e >= n) break;
-      const uint32_t u = key(e);
-      bool keep = false;
-      if (u > thr) keep = true;
-      else if (u == thr) { keep = q < take_eq; ++q; }
-      if (keep) out[pos++] = j0 + e;
-    }
+  for (int e = 0; e < n_loop; ++e) {
+    if (e >= n) break;
+    const uint32_t u = key(e);
+    bool keep = false;
+    if (u > thr) keep = true;
+    else if (u == thr) { keep = q < take_eq; ++q; }
+    if (keep && pos < lp) out[pos++] = j0 + e;
   }
 }
 
