@@ -227,6 +227,46 @@ def test_selection_across_list_lengths(L, lp):
     check_idx(want, idx.cpu().numpy(), O.select_passing(want, lp), lp)
 
 
+def test_selection_with_zero_and_equal_scores():
+    # Lists the radix passes of the top-lp kernel meet at their extremes:
+    # block 0 of KV head 0 scores 70 % of its keys exactly 0 (their logits lie
+    # thousands below every query row's maximum, so exp underflows in float32
+    # and float64 alike) and keeps more keys than score above 0, so the
+    # threshold is 0 and the kept zeros are the lowest-indexed ones, with
+    # the full 32-bit range of order keys to split; block 1 of KV head 0
+    # holds one key repeated, so every score is equal and the kernel takes
+    # the lp lowest indices without a radix pass; the other lists are drawn
+    # as usual.
+    w = W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=0, V=3, L=1500, n_q=6, lp=600, seed=41)
+    x = W.make_inputs(w)
+    G, L, n0 = w.group, w.host_len, w.n_tokens - w.n_query
+    x["q16"][n0:, :G] &= np.uint16(0x7FFF)                   # query rows of group 0: |q|
+    x["q"][n0:, :G] = np.abs(x["q"][n0:, :G])
+    rng = np.random.default_rng(41)
+    bad = rng.choice(L, int(0.7 * L), replace=False)
+    x["k"][bad, 0] = -512.0                                 # block 0, KV head 0
+    x["k16"][bad, 0] = W.bf16_bits(np.full(w.head_dim, -512.0, np.float32))
+    x["k"][L:2 * L, 0] = x["k"][L + 7, 0]                   # block 1, KV head 0: one key
+    x["k16"][L:2 * L, 0] = x["k16"][L + 7, 0]
+    plan = S.plan_for(w)
+    q, k, _ = dev_inputs(x, w)
+    ws = torch.empty(S.spava_score_topk_ws_bytes(plan), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((w.n_hosts, w.n_kv_heads, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.n_hosts, w.n_kv_heads, w.lp), dtype=torch.int32, device="cuda")
+    S.spava_score_topk(plan, q, k, scores, idx, ws)
+    torch.cuda.synchronize()
+    want = O.block_scores(x["q"], x["k"], w.n_anchor, w.n_hosts, w.host_len, w.n_query)
+    assert (want[0, 0, bad] == 0).all() and (want[0, 0] > 0).sum() < w.lp
+    assert (want[1, 0] == want[1, 0, 0]).all()
+    got = np64(scores)
+    assert (got[0, 0, bad] == 0).all() and (got[1, 0] == got[1, 0, 0]).all()
+    err = np.abs(got - want) / np.maximum(np.abs(want), 1e-30)
+    assert err.max() < 1e-5, f"scores rel err {err.max():.2e}"
+    sel = O.select_passing(want, w.lp)
+    np.testing.assert_array_equal(idx.cpu().numpy()[:2, 0], sel[:2, 0])   # ties: exact
+    check_idx(want, idx.cpu().numpy(), sel, w.lp)
+
+
 @pytest.mark.parametrize("d,L", [(64, 1000), (128, 777)])
 def test_column_sums_on_a_large_grid(d, L):
     # V * Hkv * ceil(L / 256) >= 1024 column-sum workgroups: the form with
