@@ -124,6 +124,12 @@ def merge_cases(count=40, seed=77):
         pad_row = int(rng.choice([0, 0, 4, 36]))     # extra elements per output row
         pad_lse = int(rng.choice([0, 0, 3, 50]))     # extra elements per LSE head row
         out.append((i, P, R, H, D, bf16, pad_row, pad_lse))
+    # Grids of at least 512 workgroups (R*H*D/4 >= 131072 threads), which
+    # take the shallow load ring (two partials in flight), with partition
+    # counts below, at and above the ring's depth, odd and even.
+    out += [(count, 1, 1024, 16, 128, True, 0, 0), (count + 1, 2, 1024, 16, 128, False, 4, 3),
+            (count + 2, 3, 700, 28, 128, True, 36, 0), (count + 3, 5, 600, 32, 64, False, 0, 50),
+            (count + 4, 9, 512, 32, 132, True, 0, 0)]
     return out
 
 
