@@ -46,14 +46,15 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 // m the maximum so far.  The sums run in partial order, so the result is
 // deterministic.
 //
-// The loads of the next PF partials are in flight while one is merged.  The
-// partials of one (row, head) lie n_rows*n_heads*d*4 bytes apart (7 MiB at
-// the 256K frame shape), so every partial in flight is another far-apart
-// region per wave; a shallow ring (PF = 2) keeps the chip's reads in few
-// DRAM regions at a time and reads faster than issuing a dozen partials at
-// once (68 % against 59 % of HBM bandwidth at 33 partials).  Grids too small
-// to fill the chip twice over take a deeper ring (PF = 8) so that enough
-// bytes are in flight.
+// A ring of PF slots keeps PF partials' loads in flight: each slot is
+// refilled with partial p + PF right after partial p is merged.  The partials
+// of one (row, head) lie n_rows*n_heads*d*4 bytes apart (7 MiB at the 256K
+// frame shape), so every partial in flight is another far-apart region per
+// wave.  A shallow ring (PF = 2) keeps the chip's reads in few DRAM regions
+// at a time, and reads faster than issuing a dozen partials at once (67 %
+// against 59 % of HBM bandwidth at 33 partials).  Grids of fewer than two
+// workgroups per CU take a deeper ring (PF = 8) so that enough bytes are in
+// flight.
 // ---------------------------------------------------------------------------
 template <int PF>
 __global__ __launch_bounds__(256) void merge_kernel(int P, int R, int H, int D,
