@@ -227,7 +227,8 @@ def test_selection_across_list_lengths(L, lp):
     check_idx(want, idx.cpu().numpy(), O.select_passing(want, lp), lp)
 
 
-def test_selection_with_zero_and_equal_scores():
+@pytest.mark.parametrize("L", [1500, 9000, 17000])
+def test_selection_with_zero_and_equal_scores(L):
     # Lists the radix passes of the top-lp kernel meet at their extremes:
     # block 0 of KV head 0 scores 70 % of its keys exactly 0 (their logits lie
     # thousands below every query row's maximum, so exp underflows in float32
@@ -236,10 +237,11 @@ def test_selection_with_zero_and_equal_scores():
     # the full 32-bit range of order keys to split; block 1 of KV head 0
     # holds one key repeated, so every score is equal and the kernel takes
     # the lp lowest indices without a radix pass; the other lists are drawn
-    # as usual.
-    w = W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=0, V=3, L=1500, n_q=6, lp=600, seed=41)
+    # as usual.  The list lengths take the kernel's 4- and 16-keys-per-thread
+    # register paths and the path that re-reads the list per pass.
+    w = W.small_workload("bf16", Hq=4, Hkv=2, d=64, la=0, V=3, L=L, n_q=6, lp=int(0.4 * L), seed=41)
     x = W.make_inputs(w)
-    G, L, n0 = w.group, w.host_len, w.n_tokens - w.n_query
+    G, n0 = w.group, w.n_tokens - w.n_query
     x["q16"][n0:, :G] &= np.uint16(0x7FFF)                   # query rows of group 0: |q|
     x["q"][n0:, :G] = np.abs(x["q"][n0:, :G])
     rng = np.random.default_rng(41)
